@@ -1,0 +1,147 @@
+"""Planted mistakes: the oracle's pins must catch each of them.
+
+Each case copies ``oracle/oracle.c``, changes one line the way a plausible
+slip would (a dropped term, a wrong sign or index, a swapped operand, an
+off-by-one mask), builds that copy with gcc into a temporary directory and
+runs a battery of the pins against it.  The mutated copy must fail at least
+one pin.  The mutations live only in the temporary copies.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from online_softmax_tiled_amd import workloads as wl
+from test_oracle_pins import brute_force, golden
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "dropped_scale": ("s *= J->scale;", "s *= 1.0;"),
+    "no_max_subtraction": ("double w = exp(sc[j] - m);", "double w = exp(sc[j]);"),
+    "wrong_group_index": ("int64_t g = h / (J->H / J->Hkv);\n    const double *qr",
+                          "int64_t g = h % J->Hkv;\n    const double *qr"),
+    "causal_off_by_one": ("if (J->causal && j > p) return 0;", "if (J->causal && j >= p) return 0;"),
+    "window_off_by_one": ("if (W > 0 && j <= p - W) return 0;", "if (W > 0 && j < p - W) return 0;"),
+    "top_left_alignment": ("int64_t p = i + (J->Nk - J->Nq);", "int64_t p = i;"),
+    "cap_not_rescaled": ("s = J->softcap * tanh(s / J->softcap);", "s = tanh(s / J->softcap);"),
+    "keys_read_from_values": ("const double *kr = J->k +", "const double *kr = J->v +"),
+    "dropped_first_product": ("for (int64_t c = 0; c < J->d; ++c) s += qr[c] * kr[c];",
+                              "for (int64_t c = 1; c < J->d; ++c) s += qr[c] * kr[c];"),
+    "unweighted_values": ("            for (int64_t c = 0; c < J->d; ++c) num[c] += w * vr[c];\n        }\n    }\n    write_row",
+                          "            for (int64_t c = 0; c < J->d; ++c) num[c] += vr[c];\n        }\n    }\n    write_row"),
+    "lse_without_log": ("if (J->lse) J->lse[out] = m + log(l);", "if (J->lse) J->lse[out] = m + l;"),
+    "stream_no_rescale": ("double corr = (run_max == -INFINITY) ? 0.0 : exp(run_max - new_max);",
+                          "double corr = 1.0;"),
+    "merge_sign_flip": ("double w_run = exp(m_run - m) * l_run;", "double w_run = exp(m - m_run) * l_run;"),
+    "merge_unnormalised": ("orow[c] = (w_run / l) * orow[c] + (w_s / l) * os[c];",
+                           "orow[c] = w_run * orow[c] + w_s * os[c];"),
+}
+
+
+def _battery(lib):
+    """Run the pins against ``lib``; return the names of those that fail."""
+    failed = []
+
+    def check(name, fn):
+        try:
+            with np.errstate(all="ignore"):
+                ok = fn()
+        except Exception:
+            ok = False
+        if not ok:
+            failed.append(name)
+
+    A = lambda *a, **kw: oracle.attention(*a, lib=lib, **kw)  # noqa: E731
+    g = golden("worked_example.json")
+    we = wl.worked_example(d=2)
+
+    def worked_example():
+        r = A(we["q"], we["k"], we["v"], 1.0)
+        return (np.all(np.abs(r["o"] - 30.0) < g["tolerance"])
+                and abs(r["lse"][0, 0, 0] - (1000 + math.log(10))) < 1e-10)
+
+    def worked_example_tiles():
+        return all(np.all(np.abs(A(we["q"], we["k"], we["v"], 1.0, tile=t)["o"] - 30.0) < 1e-10)
+                   for t in (1, 2, 4))
+
+    rng = np.random.default_rng(7)
+    q, k, v = rng.standard_normal((1, 4, 4, 3)), rng.standard_normal((1, 2, 6, 3)), rng.standard_normal((1, 2, 6, 3))
+    hw = [0, 2, 3, 0]
+
+    def brute():
+        o_ref, lse_ref = brute_force(q, k, v, 0.8, True, hw, 1.5)
+        r = A(q, k, v, 0.8, causal=True, head_window=hw, softcap=1.5)
+        return np.allclose(r["o"], o_ref, atol=1e-12) and np.allclose(r["lse"], lse_ref, atol=1e-12)
+
+    def uniform_counts():
+        z = np.zeros((1, 4, 4, 3))
+        r = A(z, k, v, 1.0, causal=True, head_window=hw)
+        for h in range(4):
+            for i in range(4):
+                p = i + 2
+                lo = max(0, p - hw[h] + 1) if hw[h] > 0 else 0
+                if abs(r["lse"][0, h, i] - math.log(p + 1 - lo)) > 1e-13:
+                    return False
+                if not np.allclose(r["o"][0, h, i], v[0, h // 2, lo:p + 1].mean(0), atol=1e-14):
+                    return False
+        return True
+
+    def softcap_values():
+        gs = golden("softcap_values.json")
+        for c in gs["cases"]:
+            qq = np.array([[[[c["logit"]]]]])
+            r = A(qq, np.ones((1, 1, 1, 1)), np.ones((1, 1, 1, 1)), 1.0, softcap=gs["kappa"])
+            if not abs(r["lse"][0, 0, 0] - c["capped"]) <= c["tolerance"]:
+                return False
+        return True
+
+    def gqa():
+        r = A(q, k, v, 0.8, causal=True)
+        r2 = A(q, np.repeat(k, 2, 1), np.repeat(v, 2, 1), 0.8, causal=True)
+        return np.allclose(r["o"], r2["o"], atol=0)
+
+    def merge_exercise():
+        gm = golden("merge_exercise.json")
+        o, lse = oracle.combine(np.array([[[1.0, 0.0], [0.0, 1.0]]]),
+                                np.array([[gm["m1"], gm["m2"]]]),
+                                np.array([[gm["l1"], gm["l2"]]]), lib=lib)
+        return (abs(math.exp(lse[0] - 5.0) - gm["expected_l"]) < gm["tolerance"]
+                and abs(o[0].sum() - 1.0) < 1e-12)
+
+    def split_invariance():
+        full = A(q, k, v, 0.8)
+        op, mp, lp = oracle.split_partials(q, k, v, 0.8, 3, lib=lib)
+        o, lse = oracle.combine(op, mp, lp, lib=lib)
+        return np.allclose(o, full["o"], atol=1e-13) and np.allclose(lse, full["lse"], atol=1e-13)
+
+    def tiling():
+        d = A(q, k, v, 0.8, causal=True)
+        return all(np.allclose(A(q, k, v, 0.8, causal=True, tile=t)["o"], d["o"], atol=1e-13)
+                   for t in (1, 2, 4))
+
+    for name, fn in [("worked_example", worked_example), ("worked_example_tiles", worked_example_tiles),
+                     ("brute_force", brute), ("uniform_counts", uniform_counts),
+                     ("softcap_values", softcap_values), ("gqa", gqa),
+                     ("merge_exercise", merge_exercise), ("split_invariance", split_invariance),
+                     ("tiling", tiling)]:
+        check(name, fn)
+    return failed
+
+
+def test_unmutated_oracle_passes_the_battery():
+    assert _battery(oracle._load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    before, after = MUTANTS[name]
+    assert src.count(before) == 1, f"mutation site for {name} not found once in oracle.c"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(before, after))
+    lib = oracle.load_variant(oracle.build(out=str(tmp_path / "liboracle_mutant.so"), src=str(mutated)))
+    failed = _battery(lib)
+    assert failed, f"planted mistake {name} passed every pin"
