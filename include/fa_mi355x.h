@@ -1,0 +1,169 @@
+/*
+ * fa_mi355x.h -- C ABI of libfa_mi355x.so: exact tiled softmax attention
+ * (FlashAttention-style forward) on AMD MI355X (gfx950).
+ *
+ * The operation (Transformers & Math, Module 16, sections 16.1-16.2; the
+ * notebook "Online Softmax Without the Attention Matrix"):
+ *
+ *     O = softmax(s) V,   s_ij = scale * <q_i, k_j>  (optionally soft-capped),
+ *
+ * computed by streaming tiles of K and V through on-chip memory while each
+ * query row keeps a running maximum m, normaliser l and unnormalised output,
+ * rescaling both by exp(m_old - m_new) when the maximum grows, so the
+ * Nq x Nk score matrix is never written to memory.  The result equals the
+ * direct softmax up to rounding.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers: device pointers (HBM), caller-allocated and caller-owned.  The
+ *   library never allocates, frees or synchronises, keeps no state between
+ *   calls and is safe to call from several host threads.
+ * Layouts: row-major, contiguous, no padding:
+ *   q, o       [B, H,   Nq, d]
+ *   k, v       [B, Hkv, Nk, d]
+ *   lse        [B, H,   Nq]           fp32, natural log of sum_j e^(s_ij)
+ *   o_part     [B, H,   Nq, S, d]     fp32 (split-KV partial outputs)
+ *   m_part,
+ *   l_part     [B, H,   Nq, S]        fp32
+ * Heads: query head h reads key/value head g = h / (H / Hkv) (consecutive
+ *   groups of H/Hkv query heads share one K/V head); H % Hkv must be 0.
+ * Positions: query row i sits at absolute position p = i + (Nk - Nq), i.e.
+ *   the last query is aligned with the last key.  causal != 0 keeps keys
+ *   j <= p.  window > 0 (only with causal) also drops keys j <= p - window,
+ *   leaving exactly the `window` most recent keys including position p
+ *   (Transformers & Math section 16.3, sliding-window attention; the causal
+ *   mask uses each token's position in the full sequence, section 16.2).
+ * Soft-cap: softcap > 0 replaces every score z by softcap * tanh(z/softcap)
+ *   (Transformers & Math section 16.5) before masking; softcap == 0 turns it
+ *   off.
+ * Degenerate inputs: B, H or Nq == 0 is a no-op returning FA_OK.  A query
+ *   row with no visible key (Nk == 0, or more queries than keys under a
+ *   causal mask) gets O = 0 and lse = -inf, as a zero normaliser leaves the
+ *   output at zero (oxios_kernel flash_attention.rs, attention).
+ * Streams: every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *   null stream).  Errors found before launch return a negative status and
+ *   launch nothing; FA_ERR_HIP reports a failed launch (hipGetLastError).
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same underlying type as hipStream_t, without pulling in HIP headers. */
+typedef struct ihipStream_t *fa_stream_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* bad size, null pointer, bad flag combination */
+    FA_ERR_UNSUPPORTED = -2, /* valid request with no kernel (d, dtype)       */
+    FA_ERR_HIP = -3          /* the HIP runtime reported a launch failure     */
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
+
+/* Head sizes with kernels: d in {32, 64, 128}. */
+#define FA_MAX_HEAD_WINDOWS 256 /* largest H accepted with per-head windows */
+
+/*
+ * fa_fwd -- bf16 forward attention, fp32 accumulation, bf16 output.
+ *
+ * q, k, v: bf16 device tensors in the layouts above.  o: bf16 [B,H,Nq,d],
+ * written with round-to-nearest-even.  lse: fp32 [B,H,Nq] or NULL (not
+ * written).  scale multiplies q.k before the soft-cap (use 1/sqrt(d) for the
+ * usual scaled dot product, nx_flashattn_scale.nx and Transformers & Math
+ * section 16.5).  causal: 0/1.  window: 0 = none, > 0 needs causal.
+ * softcap: 0 = none, > 0 = cap value.
+ * Errors: FA_ERR_INVALID_ARG for negative sizes, Hkv < 1, H % Hkv != 0, a
+ * NULL q/k/v/o when the tensor is non-empty, window < 0, window > 0 without
+ * causal, softcap < 0 or non-finite, non-finite scale; FA_ERR_UNSUPPORTED
+ * for d not in {32, 64, 128}.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+           float scale, int causal, int window, float softcap, fa_stream_t stream);
+
+/*
+ * fa_fwd_f32 -- the same operation on fp32 tensors (q, k, v, o fp32), with
+ * fp32 arithmetic throughout.  Arguments and errors as fa_fwd.
+ */
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+               int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+               float scale, int causal, int window, float softcap, fa_stream_t stream);
+
+/*
+ * fa_fwd_ex -- fa_fwd / fa_fwd_f32 with a window per query head, as when
+ * local (sliding-window) and global heads alternate (Transformers & Math
+ * section 16.3, alternating local and global attention).
+ *
+ * dtype selects bf16 (FA_DTYPE_BF16) or fp32 (FA_DTYPE_FP32) tensors.
+ * head_window: NULL (every head uses `window`) or a HOST array of H int32
+ * values, each 0 (no window) or > 0; read during the call only.  H may be at
+ * most FA_MAX_HEAD_WINDOWS when head_window is given (else
+ * FA_ERR_UNSUPPORTED).  A positive entry needs causal.
+ */
+typedef struct fa_fwd_args {
+    int dtype;
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int64_t B, H, Hkv, Nq, Nk, d;
+    float scale;
+    int causal;
+    int window;
+    float softcap;
+    const int32_t *head_window;
+    fa_stream_t stream;
+} fa_fwd_args;
+
+int fa_fwd_ex(const fa_fwd_args *args);
+
+/*
+ * fa_fwd_splitkv -- split-KV attention, first pass (bf16 q, k, v).
+ *
+ * The keys are cut into num_splits chunks of C = ceil(Nk / num_splits) keys;
+ * split s covers keys [s*C, min(Nk, (s+1)*C)).  For every query row and split
+ * it writes the split's own result, the per-block state of the merge rule
+ * in Transformers & Math section 16.2:
+ *   m_part[.., s] = max of the row's visible scores in the chunk (-inf if none),
+ *   l_part[.., s] = sum over those keys of exp(score - m_part) (0 if none),
+ *   o_part[.., s, :] = that chunk's normalised output (0 if none),
+ * all fp32, scores in natural-log units (after scale and soft-cap).
+ * fa_combine merges them.  Masks, soft-cap and GQA as fa_fwd; num_splits >= 1.
+ * Errors as fa_fwd, plus FA_ERR_INVALID_ARG for num_splits < 1 or NULL
+ * partial pointers when B*H*Nq > 0.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v,
+                   float *o_part, float *m_part, float *l_part,
+                   int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                   float scale, int causal, int window, float softcap, int num_splits,
+                   fa_stream_t stream);
+
+/*
+ * fa_combine -- merge per-split results into the final output.
+ *
+ * For each row: m = max_s m_s, l = sum_s e^(m_s - m) l_s,
+ * O = sum_s (e^(m_s - m) l_s / l) O_s, lse = m + ln l: the two-block merge
+ * equations of Transformers & Math section 16.2 applied to all splits at
+ * once (splits with l_s = 0 carry no weight).  o: [B,H,Nq,d] in out_dtype
+ * (FA_DTYPE_BF16, round-to-nearest-even, or FA_DTYPE_FP32).  lse: fp32
+ * [B,H,Nq] or NULL.  A row whose splits are all empty gets O = 0,
+ * lse = -inf.  Errors: FA_ERR_INVALID_ARG for negative sizes, num_splits < 1,
+ * NULL inputs/o when non-empty, unknown out_dtype; FA_ERR_UNSUPPORTED for d
+ * not in {32, 64, 128}.
+ */
+int fa_combine(const float *o_part, const float *m_part, const float *l_part,
+               void *o, float *lse, int64_t B, int64_t H, int64_t Nq, int64_t d,
+               int num_splits, int out_dtype, fa_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

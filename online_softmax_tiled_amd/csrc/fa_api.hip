@@ -1,0 +1,171 @@
+// fa_api.hip -- the extern "C" entry points of libfa_mi355x.so declared in
+// include/fa_mi355x.h: argument validation, then one or two kernel launches
+// on the caller's stream.  No allocation, no synchronisation, no state.
+#include <math.h>
+#include <string.h>
+
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace {
+
+using fa::FwdParams;
+
+bool supported_d(int64_t d) { return d == 32 || d == 64 || d == 128; }
+
+// Checks shared by every forward entry point.  Fills p on success.
+int validate_fwd(const fa_fwd_args &a, FwdParams &p) {
+    if (a.B < 0 || a.H < 0 || a.Hkv < 1 || a.Nq < 0 || a.Nk < 0 || a.d < 0) return FA_ERR_INVALID_ARG;
+    if (a.H % a.Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (!isfinite(a.scale)) return FA_ERR_INVALID_ARG;
+    if (!isfinite(a.softcap) || a.softcap < 0.0f) return FA_ERR_INVALID_ARG;
+    if (a.window < 0) return FA_ERR_INVALID_ARG;
+    if (a.window > 0 && !a.causal) return FA_ERR_INVALID_ARG;
+    if (a.dtype != FA_DTYPE_BF16 && a.dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
+    if (a.head_window) {
+        if (a.H > FA_MAX_HEAD_WINDOWS) return FA_ERR_UNSUPPORTED;
+        for (int64_t h = 0; h < a.H; ++h) {
+            if (a.head_window[h] < 0) return FA_ERR_INVALID_ARG;
+            if (a.head_window[h] > 0 && !a.causal) return FA_ERR_INVALID_ARG;
+        }
+    }
+    const bool q_nonempty = a.B * a.H * a.Nq * a.d > 0;
+    const bool kv_nonempty = a.B * a.Hkv * a.Nk * a.d > 0;
+    if (q_nonempty && (!a.q || !a.o)) return FA_ERR_INVALID_ARG;
+    if (kv_nonempty && (!a.k || !a.v)) return FA_ERR_INVALID_ARG;
+    if (!supported_d(a.d)) return FA_ERR_UNSUPPORTED;
+    if (a.H / a.Hkv > 0x7fffffff || a.Nq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+
+    memset(&p, 0, sizeof p);
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.o = a.o;
+    p.lse = a.lse;
+    p.B = a.B;
+    p.H = a.H;
+    p.Hkv = a.Hkv;
+    p.Nq = a.Nq;
+    p.Nk = a.Nk;
+    p.group = (int)(a.H / a.Hkv);
+    p.num_splits = 1;
+    p.split_len = 0;
+    p.scale = a.scale;
+    p.softcap = a.softcap;
+    p.causal = a.causal ? 1 : 0;
+    p.window = a.window;
+    if (a.head_window) {
+        p.has_head_window = 1;
+        for (int64_t h = 0; h < a.H; ++h) p.head_window[h] = a.head_window[h];
+    }
+    return FA_OK;
+}
+
+int run_fwd(const fa_fwd_args &a) {
+    FwdParams p;
+    const int rc = validate_fwd(a, p);
+    if (rc != FA_OK) return rc;
+    if (a.B == 0 || a.H == 0 || a.Nq == 0) return FA_OK;
+    hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
+    if (a.dtype == FA_DTYPE_FP32) return fa::launch_fwd_f32(p, (int)a.d, s);
+    return fa::launch_fwd_bf16(p, (int)a.d, false, s);
+}
+
+fa_fwd_args make_args(int dtype, const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                      int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                      int window, float softcap, fa_stream_t stream) {
+    fa_fwd_args a;
+    memset(&a, 0, sizeof a);
+    a.dtype = dtype;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal;
+    a.window = window;
+    a.softcap = softcap;
+    a.head_window = nullptr;
+    a.stream = stream;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t Hkv,
+           int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int window, float softcap,
+           fa_stream_t stream) {
+    return run_fwd(make_args(FA_DTYPE_BF16, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap,
+                             stream));
+}
+
+int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int64_t B, int64_t H,
+               int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, int window, float softcap,
+               fa_stream_t stream) {
+    return run_fwd(make_args(FA_DTYPE_FP32, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap,
+                             stream));
+}
+
+int fa_fwd_ex(const fa_fwd_args *args) {
+    if (!args) return FA_ERR_INVALID_ARG;
+    return run_fwd(*args);
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o_part, float *m_part, float *l_part,
+                   int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                   int window, float softcap, int num_splits, fa_stream_t stream) {
+    if (num_splits < 1) return FA_ERR_INVALID_ARG;
+    // o is not written by this pass; validate with a stand-in so only the
+    // partial pointers are required.
+    fa_fwd_args a = make_args(FA_DTYPE_BF16, q, k, v, o_part, nullptr, B, H, Hkv, Nq, Nk, d, scale, causal,
+                              window, softcap, stream);
+    FwdParams p;
+    const int rc = validate_fwd(a, p);
+    if (rc != FA_OK) return rc;
+    if (B * H * Nq > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
+    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    const int64_t split_len = (Nk + num_splits - 1) / num_splits;
+    if (split_len > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    p.o = nullptr;
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+    p.num_splits = num_splits;
+    p.split_len = (int)split_len;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((int64_t)p.group * Nq <= fa::splitkv_decode_max_rows()) return fa::launch_splitkv_decode(p, (int)d, s);
+    return fa::launch_fwd_bf16(p, (int)d, true, s);
+}
+
+int fa_combine(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse, int64_t B,
+               int64_t H, int64_t Nq, int64_t d, int num_splits, int out_dtype, fa_stream_t stream) {
+    if (B < 0 || H < 0 || Nq < 0 || d < 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
+    if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
+    const int64_t rows = B * H * Nq;
+    if (rows > 0 && d > 0 && (!o_part || !m_part || !l_part || !o)) return FA_ERR_INVALID_ARG;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    if (rows == 0) return FA_OK;
+    return fa::launch_combine(o_part, m_part, l_part, o, lse, rows, num_splits, (int)d, out_dtype,
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
+const char *fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this head size or shape";
+        case FA_ERR_HIP: return "FA_ERR_HIP: HIP kernel launch failed";
+        default: return "unknown fa_status";
+    }
+}
+
+}  // extern "C"

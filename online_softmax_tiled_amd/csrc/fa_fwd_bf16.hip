@@ -1,0 +1,361 @@
+// fa_fwd_bf16.hip -- bf16 tiled forward attention with an online softmax,
+// MFMA (v_mfma_f32_32x32x16_bf16) for both contractions, gfx950.
+//
+// The method (Transformers & Math, Module 16, section 16.1 flow and 16.2
+// merge rule): a workgroup loads one block of query rows, streams blocks of
+// K and V through LDS, computes that block's scores, updates each row's
+// running maximum and sum, adds the block's contribution to an output kept
+// on chip, and writes the finished output once.  The score matrix never
+// reaches HBM.
+//
+// Tiling on CDNA4:
+//   * workgroup = 4 waves = 128 query rows (32 per wave); key tiles of 64.
+//   * scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T
+//     kept in registers), so the 32x32 accumulator gives every lane ONE
+//     query row and 16 of its keys; the partner lane (lane ^ 32) holds the
+//     other 16.  Row max / row sum are in-lane reductions plus one swap.
+//   * the output is accumulated transposed, O^T += V^T P^T: the score
+//     accumulator registers, rounded to bf16, are exactly the B operand
+//     (keys permuted consistently with the V^T read), and each lane again
+//     owns one query row, so the rescale by exp(m_old - m_new) is a per-lane
+//     multiply.
+//   * K is staged row-major and V transposed (key-contiguous) in LDS, both
+//     padded so the MFMA operand reads are bank-conflict free; two LDS
+//     stages: the next tile's global loads are in flight while the current
+//     tile is computed.
+//   * blocks are ordered so that all query tiles of one K/V head run back to
+//     back on the same XCD (shared L2), the longest causal tiles first.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int BM = 128;  // query rows per workgroup
+constexpr int BN = 64;   // keys per tile
+constexpr int NT = 256;  // threads per workgroup
+
+template <int D>
+struct Smem {
+    static constexpr int KSTR = D + 8;   // bf16 per K row in LDS (16 B pad)
+    static constexpr int VSTR = BN + 4;  // bf16 per V^T row in LDS (8 B pad)
+    static constexpr int KTILE = BN * KSTR;
+    static constexpr int VTILE = D * VSTR;
+    static constexpr int STAGE = KTILE + VTILE;
+    static constexpr int KCH = BN * D / 8 / NT;   // 16-B K chunks per thread
+    static constexpr int VUNITS = (BN / 4) * (D / 8);  // 4 keys x 8 dims units
+};
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Pick two bf16 halves: (lo half of a, lo half of b) or (hi of a, hi of b).
+__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
+    return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+// Block index -> (query tile, head, batch, split).  The unit of locality is
+// one (batch, K/V head): its query heads and tiles are consecutive in the
+// dispatch order of one XCD (block ids are dealt round-robin over 8 XCDs).
+struct Work {
+    int qtile, h, b, split;
+};
+
+__device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
+    const int bid = blockIdx.x;
+    const int rep = p.group, S = p.num_splits;
+    const int units = (int)(p.B * p.Hkv);
+    const int per_unit = rep * n_qtiles * S;
+    int unit, r;
+    if (units % 8 == 0) {
+        const int x = bid & 7, s = bid >> 3;
+        unit = (s / per_unit) * 8 + x;
+        r = s % per_unit;
+    } else {
+        unit = bid % units;
+        r = bid / units;
+    }
+    Work w;
+    const int hg = r % rep;
+    const int rest = r / rep;
+    w.split = rest % S;
+    const int rank = rest / S;
+    w.qtile = p.causal ? (n_qtiles - 1 - rank) : rank;
+    w.b = unit / (int)p.Hkv;
+    w.h = (unit % (int)p.Hkv) * rep + hg;
+    return w;
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, const int n_qtiles) {
+    using L = Smem<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const Work w = decode_block(p, n_qtiles);
+    const int h = w.h, b = w.b;
+    const int g = h / p.group;
+    const int64_t Nq = p.Nq, Nk = p.Nk;
+    const int64_t off = Nk - Nq;
+    const int W = head_window_of(p, h);
+
+    // Key range of this split (the whole key axis unless split-KV).
+    int64_t r_lo = 0, r_hi = Nk;
+    if (SPLIT) {
+        r_lo = (int64_t)w.split * p.split_len;
+        r_hi = r_lo + p.split_len < Nk ? r_lo + p.split_len : Nk;
+        if (r_lo > Nk) r_lo = Nk;
+    }
+
+    const int64_t q0 = (int64_t)w.qtile * BM;
+    const int64_t qlast = (q0 + BM < Nq ? q0 + BM : Nq) - 1;
+    int64_t lo_first, hi_first, lo_last, hi_last;
+    key_bounds(q0 + off, Nk, p.causal, W, lo_first, hi_first);
+    key_bounds(qlast + off, Nk, p.causal, W, lo_last, hi_last);
+    // Union of the rows' visible keys, and the part every row sees.
+    const int64_t kbeg = lo_first > r_lo ? lo_first : r_lo;
+    const int64_t kend = hi_last < r_hi ? hi_last : r_hi;
+    const int64_t full_lo = lo_last > r_lo ? lo_last : r_lo;
+    const int64_t full_hi = hi_first < r_hi ? hi_first : r_hi;
+
+    // This lane's query row and its own visible interval.
+    const int64_t qrow = q0 + wave * 32 + l32;
+    int64_t kmin, kmax;
+    {
+        int64_t lo, hi;
+        key_bounds(qrow + off, Nk, p.causal, W, lo, hi);
+        kmin = lo > r_lo ? lo : r_lo;
+        kmax = hi < r_hi ? hi : r_hi;
+    }
+
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.H + h) * Nq * D;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * Nk * D;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * Nk * D;
+
+    // Q^T fragments (the B operand of S^T = K Q^T): row qrow, 8 dims per step.
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (qrow < Nq) x = ldg16(Q + qrow * D + ds * 16 + hf * 8);
+        qf[ds] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    // Scores in base 2: t = s * log2(e).
+    const float c_log2 = p.scale * kLog2e;
+    const bool capped = p.softcap > 0.0f;
+
+    float m = kNegInf, l = 0.0f;
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
+
+    const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
+
+    u32x4 kreg[L::KCH];
+    u32x4 vreg[4];
+    const int vkg = tid & 15, vdc = tid >> 4;  // V unit: keys 4*vkg.., dims 8*vdc..
+
+    auto gload = [&](int64_t kt) {
+#pragma unroll
+        for (int c = 0; c < L::KCH; ++c) {
+            const int chunk = tid + NT * c;
+            const int64_t key = kt + chunk / (D / 8);
+            const int dc = chunk % (D / 8);
+            kreg[c] = key < Nk ? ldg16(K + key * D + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+        if (tid < L::VUNITS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t key = kt + vkg * 4 + r;
+                vreg[r] = key < Nk ? ldg16(V + key * D + vdc * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+        uint16_t *Ks = lds + buf * L::STAGE;
+        uint16_t *Vs = Ks + L::KTILE;
+#pragma unroll
+        for (int c = 0; c < L::KCH; ++c) {
+            const int chunk = tid + NT * c;
+            *reinterpret_cast<u32x4 *>(Ks + (chunk / (D / 8)) * L::KSTR + (chunk % (D / 8)) * 8) = kreg[c];
+        }
+        if (tid < L::VUNITS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {  // dword e of each row: dims 2e, 2e+1
+                u32x2 lo = {pick_lo(vreg[0][e], vreg[1][e]), pick_lo(vreg[2][e], vreg[3][e])};
+                u32x2 hi = {pick_hi(vreg[0][e], vreg[1][e]), pick_hi(vreg[2][e], vreg[3][e])};
+                *reinterpret_cast<u32x2 *>(Vs + (vdc * 8 + 2 * e) * L::VSTR + vkg * 4) = lo;
+                *reinterpret_cast<u32x2 *>(Vs + (vdc * 8 + 2 * e + 1) * L::VSTR + vkg * 4) = hi;
+            }
+        }
+    };
+
+    if (ntiles > 0) {
+        gload(kbeg);
+        lstore(0);
+        __syncthreads();
+    }
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t kt = kbeg + (int64_t)it * BN;
+        const int buf = it & 1;
+        if (it + 1 < ntiles) gload(kt + BN);
+
+        const uint16_t *Ks = lds + buf * L::STAGE;
+        const uint16_t *Vs = Ks + L::KTILE;
+
+        // ---- S^T = K Q^T for the 64 keys of this tile (two 32-key blocks)
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
+#pragma unroll
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(Ks + (kb * 32 + l32) * L::KSTR + ds * 16 + hf * 8);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds],
+                                                                   sacc[kb], 0, 0, 0);
+            }
+        }
+
+        // ---- scale / soft-cap, then mask (after the cap) where needed.
+        // Element j of block kb holds key kt + kb*32 + 8*(j/4) + 4*hf + (j%4).
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                sacc[kb][j] = capped ? softcap_log2(sacc[kb][j] * p.scale, p.softcap) : sacc[kb][j] * c_log2;
+
+        const bool need_mask = !(kt >= full_lo && kt + BN <= full_hi);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int64_t key = kt + kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
+                    if (key < kmin || key >= kmax) sacc[kb][j] = kNegInf;
+                }
+        }
+
+        // ---- online softmax: row max over the 64 keys (this lane's 32 + partner's 32)
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == kNegInf ? 0.0f : m_new;  // no (-inf) - (-inf)
+        const float alpha = fast_exp2(m - m_use);
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float pj = fast_exp2(sacc[kb][j] - m_use);
+                sacc[kb][j] = pj;
+                rs += pj;
+            }
+        rs += __shfl_xor(rs, 32);
+        l = l * alpha + rs;
+        m = m_new;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+
+        // ---- O^T += V^T P^T.  k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16):
+        // this lane half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
+        // exactly accumulator elements 8*gp .. 8*gp+7.
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+                u32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = pack_bf16x2(sacc[kb][8 * gp + 2 * e], sacc[kb][8 * gp + 2 * e + 1]);
+                pf[kb * 2 + gp] = __builtin_bit_cast(bf16x8, x);
+            }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const uint16_t *vrow = Vs + (db * 32 + l32) * L::VSTR + 4 * hf;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x2 a0 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16);
+                const u32x2 a1 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16 + 8);
+                const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[ks],
+                                                                   oacc[db], 0, 0, 0);
+            }
+        }
+
+        if (it + 1 < ntiles) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l.  Lane holds dims db*32 + 8*(j/4) + 4*hf + (j%4).
+    if (qrow >= Nq) return;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int64_t row = ((int64_t)b * p.H + h) * Nq + qrow;
+    if (!SPLIT) {
+        uint16_t *O = static_cast<uint16_t *>(p.o) + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                u32x2 x = {pack_bf16x2(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(O + db * 32 + 8 * gq + 4 * hf) = x;
+            }
+        if (p.lse && hf == 0) p.lse[row] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;
+    } else {
+        const int64_t prow = row * p.num_splits + w.split;
+        float *Op = p.o_part + prow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                f32x4 x = {oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv, oacc[db][4 * gq + 2] * inv,
+                           oacc[db][4 * gq + 3] * inv};
+                *reinterpret_cast<f32x4 *>(Op + db * 32 + 8 * gq + 4 * hf) = x;
+            }
+        if (hf == 0) {
+            p.m_part[prow] = l > 0.0f ? m * kLn2 : kNegInf;
+            p.l_part[prow] = l;
+        }
+    }
+}
+
+template <int D, bool SPLIT>
+int launch_one(const FwdParams &p, hipStream_t stream) {
+    const int n_qtiles = (int)((p.Nq + BM - 1) / BM);
+    const int64_t blocks = p.B * p.H * (int64_t)n_qtiles * p.num_splits;
+    if (blocks <= 0) return FA_OK;
+    if (blocks > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, SPLIT>), dim3((unsigned)blocks), dim3(NT), 0, stream, p, n_qtiles);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_fwd_bf16(const FwdParams &p, int d, bool split, hipStream_t stream) {
+    switch (d) {
+        case 32: return split ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);
+        case 64: return split ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+        case 128: return split ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+        default: return FA_ERR_UNSUPPORTED;
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,22 @@
+// fa_kernels.h -- host-side launchers of the HIP kernels (internal to
+// libfa_mi355x.so).  Each returns an fa_status; arguments are validated by
+// the C ABI layer before any launcher is called.
+#pragma once
+
+#include "fa_device.h"
+
+namespace fa {
+
+// bf16 tiled forward (MFMA).  split: write per-split partials instead of O.
+int launch_fwd_bf16(const FwdParams &p, int d, bool split, hipStream_t stream);
+// fp32 tiled forward (VALU, fp32 throughout).
+int launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream);
+// bf16 split-KV partial pass for few query rows per K/V head (decode).
+int launch_splitkv_decode(const FwdParams &p, int d, hipStream_t stream);
+// Rows of query rows per K/V head up to which the decode kernel is used.
+int splitkv_decode_max_rows();
+// Merge per-split partials into O (bf16 or fp32) and lse.
+int launch_combine(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse,
+                   int64_t rows, int num_splits, int d, int out_dtype, hipStream_t stream);
+
+}  // namespace fa

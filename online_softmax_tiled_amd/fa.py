@@ -1,0 +1,221 @@
+"""ctypes binding of libfa_mi355x.so (the C ABI in include/fa_mi355x.h).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  The raw functions (``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_ex``,
+``fa_fwd_splitkv``, ``fa_combine``) take the C arguments one to one; tensor
+arguments may be torch tensors (their ``data_ptr()`` is passed) or integer
+device addresses.  They raise :class:`FaError` on a non-zero status.
+
+``attention`` and ``splitkv_attention`` allocate the outputs with torch and
+call the raw functions with shapes taken from the tensors.
+
+The library is loaded on first use.  If it is missing the call raises: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libfa_mi355x.so"
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
+FA_MAX_HEAD_WINDOWS = 256
+
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_status_string")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fa_status_string(status)} ({status})")
+        self.status = status
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of struct fa_fwd_args."""
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("Nq", ctypes.c_int64), ("Nk", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("softcap", ctypes.c_float),
+        ("head_window", ctypes.POINTER(ctypes.c_int32)),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libfa_mi355x.so (once).  Raises FileNotFoundError if not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is not built; run `python -m online_softmax_tiled_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    fwd_args = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci, f32, vp]
+    lib.fa_fwd.argtypes = fwd_args
+    lib.fa_fwd_f32.argtypes = fwd_args
+    lib.fa_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                   f32, ci, ci, f32, ci, vp]
+    lib.fa_combine.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine"):
+        getattr(lib, name).restype = ci
+    lib.fa_status_string.argtypes = [ci]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x or None
+    return x.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _check(status: int, what: str):
+    if status != FA_OK:
+        raise FaError(status, what)
+
+
+# ------------------------------------------------------------------ raw ABI
+def fa_fwd(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap, stream=None):
+    _check(load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                                 float(scale), int(causal), int(window), float(softcap), _stream(stream)),
+           "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap, stream=None):
+    _check(load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                                     float(scale), int(causal), int(window), float(softcap), _stream(stream)),
+           "fa_fwd_f32")
+
+
+def fa_fwd_ex(dtype, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap,
+              head_window=None, stream=None):
+    hw = None
+    if head_window is not None:
+        hw = (ctypes.c_int32 * len(head_window))(*[int(x) for x in head_window])
+    a = FwdArgs(int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                float(scale), int(causal), int(window), float(softcap),
+                ctypes.cast(hw, ctypes.POINTER(ctypes.c_int32)) if hw is not None else None,
+                _stream(stream))
+    _check(load_library().fa_fwd_ex(ctypes.byref(a)), "fa_fwd_ex")
+
+
+def fa_fwd_splitkv(q, k, v, o_part, m_part, l_part, B, H, Hkv, Nq, Nk, d, scale, causal, window,
+                   softcap, num_splits, stream=None):
+    _check(load_library().fa_fwd_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(m_part), _ptr(l_part), B, H, Hkv, Nq, Nk, d,
+        float(scale), int(causal), int(window), float(softcap), int(num_splits), _stream(stream)),
+        "fa_fwd_splitkv")
+
+
+def fa_combine(o_part, m_part, l_part, o, lse, B, H, Nq, d, num_splits, out_dtype, stream=None):
+    _check(load_library().fa_combine(_ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(o), _ptr(lse),
+                                      B, H, Nq, d, int(num_splits), int(out_dtype), _stream(stream)),
+           "fa_combine")
+
+
+# ------------------------------------------------------------- conveniences
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D: [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("q [B,H,Nq,d], k and v [B,Hkv,Nk,d] shapes disagree")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    return B, H, Hkv, Nq, Nk, d
+
+
+def attention(q, k, v, scale=None, causal=False, window=0, head_window=None, softcap=0.0,
+              out=None, lse=None):
+    """O = softmax(scale * q k^T) v per head (exact, tiled).  q: [B,H,Nq,d],
+    k, v: [B,Hkv,Nk,d], bf16 or fp32 on the GPU.  Returns (o, lse)."""
+    import torch
+    B, H, Hkv, Nq, Nk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if q.dtype == torch.bfloat16:
+        dtype = FA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dtype = FA_DTYPE_FP32
+    else:
+        raise ValueError("q, k, v must be bfloat16 or float32")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if head_window is not None:
+        fa_fwd_ex(dtype, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap,
+                  head_window=head_window)
+    elif dtype == FA_DTYPE_BF16:
+        fa_fwd(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap)
+    else:
+        fa_fwd_f32(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap)
+    return o, lse
+
+
+def splitkv_attention(q, k, v, num_splits, scale=None, causal=False, window=0, softcap=0.0,
+                      out_dtype=None, partials=None, return_partials=False):
+    """Split-KV attention: per-split partials (fa_fwd_splitkv) merged by
+    fa_combine.  q, k, v bf16.  ``partials`` may pass preallocated
+    (o_part [B,H,Nq,S,d], m_part, l_part [B,H,Nq,S]) fp32 buffers."""
+    import torch
+    B, H, Hkv, Nq, Nk, d = _shapes(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("split-KV takes bfloat16 q, k, v")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    S = int(num_splits)
+    if partials is None:
+        o_part = torch.empty((B, H, Nq, S, d), dtype=torch.float32, device=q.device)
+        m_part = torch.empty((B, H, Nq, S), dtype=torch.float32, device=q.device)
+        l_part = torch.empty((B, H, Nq, S), dtype=torch.float32, device=q.device)
+    else:
+        o_part, m_part, l_part = partials
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    fa_fwd_splitkv(q, k, v, o_part, m_part, l_part, B, H, Hkv, Nq, Nk, d, scale, causal, window,
+                   softcap, S)
+    fa_combine(o_part, m_part, l_part, o, lse, B, H, Nq, d, S,
+               FA_DTYPE_BF16 if out_dtype == torch.bfloat16 else FA_DTYPE_FP32)
+    if return_partials:
+        return o, lse, (o_part, m_part, l_part)
+    return o, lse

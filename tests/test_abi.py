@@ -1,0 +1,130 @@
+"""The C ABI library: it loads, exports what include/fa_mi355x.h declares,
+its struct layout matches the binding, and argument validation rejects bad
+calls before any HIP work (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from online_softmax_tiled_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+FAKE = 0x1000  # a non-null address that validation-failing calls never touch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_is_built_and_loads():
+    assert os.path.exists(fa.library_path()), "run python -m online_softmax_tiled_amd.build"
+    fa.load_library()
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(fa.EXPORTED), names
+    lib = ctypes.CDLL(fa.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_status_strings():
+    assert fa.fa_status_string(0) == "FA_OK"
+    for s in (-1, -2, -3):
+        assert fa.fa_status_string(s).startswith("FA_ERR")
+    assert "unknown" in fa.fa_status_string(7)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fa_mi355x.h"\n'
+                   "int main(void){printf(\"%zu %zu %zu %zu\\n\", sizeof(fa_fwd_args),"
+                   " offsetof(fa_fwd_args, scale), offsetof(fa_fwd_args, head_window),"
+                   " offsetof(fa_fwd_args, stream));return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    A = fa.FwdArgs
+    assert vals == [ctypes.sizeof(A), A.scale.offset, A.head_window.offset, A.stream.offset]
+
+
+def call_fwd(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=4, Hkv=2, Nq=8, Nk=8, d=64,
+             scale=0.125, causal=0, window=0, softcap=0.0, stream=FAKE)
+    a.update(over)
+    lib = fa.load_library()
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"],
+                      a["d"], a["scale"], a["causal"], a["window"], a["softcap"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(H=3), fa.FA_ERR_INVALID_ARG),                 # H % Hkv != 0
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(window=4), fa.FA_ERR_INVALID_ARG),            # window needs causal
+    (dict(window=-1, causal=1), fa.FA_ERR_INVALID_ARG),
+    (dict(softcap=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(softcap=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=48), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_validation(over, status):
+    assert call_fwd(**over) == status
+
+
+def test_empty_is_a_no_op_without_touching_pointers():
+    # No query rows: nothing to do, so NULL tensors are fine and nothing runs.
+    assert call_fwd(Nq=0, q=None, o=None) == fa.FA_OK
+    assert call_fwd(B=0, q=None, k=None, v=None, o=None) == fa.FA_OK
+
+
+def test_splitkv_and_combine_validation():
+    lib = fa.load_library()
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 1, 64, 64, 0.1, 0, 0, 0.0]
+    assert lib.fa_fwd_splitkv(*base, 0, FAKE) == fa.FA_ERR_INVALID_ARG      # num_splits < 1
+    b2 = list(base); b2[4] = None
+    assert lib.fa_fwd_splitkv(*b2, 4, FAKE) == fa.FA_ERR_INVALID_ARG        # NULL m_part
+    b3 = list(base); b3[11] = 80
+    assert lib.fa_fwd_splitkv(*b3, 4, FAKE) == fa.FA_ERR_UNSUPPORTED        # d = 80
+    c = [FAKE, FAKE, FAKE, FAKE, None, 1, 4, 1, 64]
+    assert lib.fa_combine(*c, 0, fa.FA_DTYPE_BF16, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_combine(*c, 4, 7, FAKE) == fa.FA_ERR_INVALID_ARG            # unknown dtype
+    c2 = list(c); c2[3] = None
+    assert lib.fa_combine(*c2, 4, fa.FA_DTYPE_BF16, FAKE) == fa.FA_ERR_INVALID_ARG
+    c3 = list(c); c3[8] = 96
+    assert lib.fa_combine(*c3, 4, fa.FA_DTYPE_FP32, FAKE) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_combine(None, None, None, None, None, 0, 4, 1, 64, 4, fa.FA_DTYPE_FP32, FAKE) == fa.FA_OK
+
+
+def test_fwd_ex_validation():
+    lib = fa.load_library()
+    hw = (ctypes.c_int32 * 4)(0, 16, 0, 16)
+    a = fa.FwdArgs(fa.FA_DTYPE_BF16, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 8, 8, 64, 0.1, 0, 0, 0.0,
+                   ctypes.cast(hw, ctypes.POINTER(ctypes.c_int32)), FAKE)
+    assert lib.fa_fwd_ex(ctypes.byref(a)) == fa.FA_ERR_INVALID_ARG          # per-head window, not causal
+    hw2 = (ctypes.c_int32 * 4)(0, -3, 0, 16)
+    a.causal = 1
+    a.head_window = ctypes.cast(hw2, ctypes.POINTER(ctypes.c_int32))
+    assert lib.fa_fwd_ex(ctypes.byref(a)) == fa.FA_ERR_INVALID_ARG          # negative entry
+    a.dtype = 5
+    assert lib.fa_fwd_ex(ctypes.byref(a)) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_ex(None) == fa.FA_ERR_INVALID_ARG
+    big = (ctypes.c_int32 * 512)()
+    a2 = fa.FwdArgs(fa.FA_DTYPE_BF16, FAKE, FAKE, FAKE, FAKE, None, 1, 512, 512, 8, 8, 64, 0.1, 1, 0, 0.0,
+                    ctypes.cast(big, ctypes.POINTER(ctypes.c_int32)), FAKE)
+    assert lib.fa_fwd_ex(ctypes.byref(a2)) == fa.FA_ERR_UNSUPPORTED         # H > FA_MAX_HEAD_WINDOWS
