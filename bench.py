@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode]
+                    [--no-cpu-baseline] [--no-decode]
+
+A step is one forward pass over one batch of synthetic input:
+
+* prefill (default): ``fa_fwd`` on the causal bf16 prefill workload
+  (B=4, H=32, 4096 x 4096, d=128) -- the headline TFLOP/s figure;
+* decode (also measured in the same run unless ``--no-decode``):
+  ``fa_fwd_splitkv`` + ``fa_combine`` on the split-KV decode workload
+  (B=16, H=32, Hkv=8, Nk=32768, d=128, 16 splits), in GB/s.
+
+Inputs are seeded synthetic tensors (online_softmax_tiled_amd.workloads),
+resident in HBM before timing starts.  Kernel durations are taken with HIP
+events recorded on the stream the kernels are launched on (torch's current
+stream).  Prints ONE JSON line.  ``cpu_baseline`` times the fp64 CPU oracle
+on a bounded row sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from online_softmax_tiled_amd import workloads as wl  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)"
+PREFILL = "bf16_causal_b4_h32_n4096_d128"
+DECODE = "bf16_splitkv_decode_b16_h32kv8_nk32768_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "prefill": ["online_softmax_tiled_amd/csrc/fa_fwd_bf16.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
+    "decode": ["online_softmax_tiled_amd/csrc/fa_splitkv.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_device(inp, torch):
+    return {n: torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv"}
+
+
+def time_launches(launch, steps, warmup, torch):
+    """Run warmup + timed launches; per-launch HIP event durations (ms)."""
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record()
+        launch()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) for s, e in ev]
+    total = ev[0][0].elapsed_time(ev[-1][1])
+    return durs, total, wall
+
+
+def bench_prefill(torch, fa, steps, warmup):
+    w = wl.WORKLOADS[PREFILL]
+    t = to_device(wl.generate(w), torch)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    args = (t["q"], t["k"], t["v"], o, lse, w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.scale, int(w.causal),
+            w.window, w.softcap)
+
+    def launch():
+        fa.fa_fwd(*args)
+
+    durs, total, wall = time_launches(launch, steps, warmup, torch)
+    flops = wl.algorithmic_flops(w)
+    avg = float(np.mean(durs))
+    achieved = flops / (avg * 1e-3) / 1e12
+    traffic = measured_traffic("prefill")
+    return w, {
+        "flops": flops, "avg_ms": avg, "total_ms": total, "wall_s": wall,
+        "value": flops * steps / (total * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+
+
+def bench_decode(torch, fa, steps, warmup):
+    w = wl.WORKLOADS[DECODE]
+    t = to_device(wl.generate(w), torch)
+    S = w.num_splits
+    o_part = torch.empty((w.B, w.H, w.Nq, S, w.d), dtype=torch.float32, device="cuda")
+    m_part = torch.empty((w.B, w.H, w.Nq, S), dtype=torch.float32, device="cuda")
+    l_part = torch.empty_like(m_part)
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+
+    def split():
+        fa.fa_fwd_splitkv(t["q"], t["k"], t["v"], o_part, m_part, l_part, w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d,
+                          w.scale, int(w.causal), w.window, w.softcap, S)
+
+    def combine():
+        fa.fa_combine(o_part, m_part, l_part, o, lse, w.B, w.H, w.Nq, w.d, S, 0)
+
+    def launch():
+        split()
+        combine()
+
+    durs, total, wall = time_launches(launch, steps, warmup, torch)
+    # the split kernel alone (the dominant kernel) for the roofline
+    sdurs, _, _ = time_launches(split, steps, 2, torch)
+    nbytes = wl.algorithmic_bytes(w)
+    part_bytes = w.B * w.H * w.Nq * S * (w.d + 2) * 4
+    split_bytes = nbytes - part_bytes - (w.B * w.H * w.Nq * (w.d * 2 + 4))  # q, k, v in; partials out
+    avg_split = float(np.mean(sdurs))
+    achieved = split_bytes / (avg_split * 1e-3) / 1e9
+    return w, {
+        "bytes": nbytes, "avg_ms": float(np.mean(durs)), "total_ms": total, "wall_s": wall,
+        "value": nbytes * steps / (total * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
+                     "kernel": "splitkv_decode_kernel", "avg_ms": round(avg_split, 4)},
+    }
+
+
+def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
+    """Time the fp64 oracle on a strided row sample of workload ``w``."""
+    import oracle
+    inp = wl.generate(w)
+    q, k, v = (inp[n].astype(np.float64) for n in "qkv")
+    total = w.B * w.H * w.Nq
+    threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    hw = list(w.head_window) if w.head_window else None
+    counts = np.broadcast_to(wl.visible_counts(w)[None], (w.B, w.H, w.Nq)).reshape(-1)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w.scale, causal=w.causal, window=w.window, head_window=hw,
+                         softcap=w.softcap, rows=rows, nthreads=threads)
+        return time.perf_counter() - t0
+
+    stride = max(1, total // 2048)
+    pilot = np.arange(0, total, stride, dtype=np.int64)
+    tp = run(pilot)
+    stride = max(1, int(stride * tp / target_s))
+    rows = np.arange(0, total, stride, dtype=np.int64)
+    secs = run(rows)
+    flops = 4 * w.d * int(counts[rows].sum())
+    if w.num_splits:
+        value, unit = wl.algorithmic_bytes(w) * len(rows) / total / secs / 1e9, "GB/s"
+    else:
+        value, unit = flops / secs / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"every {stride}th query row of {w.name} ({len(rows)} of {total} rows, "
+                      f"{flops / 1e9:.1f} GFLOP fp64 in {secs:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["prefill", "decode"], default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").random_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}))
+        return
+    import online_softmax_tiled_amd as fa
+    fa.load_library()
+    torch.cuda.init()
+
+    main_w, leg = None, None
+    decode = None
+    if args.workload == "prefill":
+        main_w, leg = bench_prefill(torch, fa, args.steps, args.warmup)
+        print(f"[bench] prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
+        if not args.no_decode:
+            dw, decode = bench_decode(torch, fa, args.steps, args.warmup)
+            print(f"[bench] decode done: {decode['avg_ms']:.3f} ms/step", file=sys.stderr, flush=True)
+        value, unit = leg["value"], "TFLOP/s"
+    else:
+        main_w, leg = bench_decode(torch, fa, args.steps, args.warmup)
+        value, unit = leg["value"], "GB/s"
+        print(f"[bench] decode done: {leg['avg_ms']:.3f} ms/step", file=sys.stderr, flush=True)
+
+    w = main_w
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(leg["total_ms"] / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "num_splits": w.num_splits or None, "parallelism": "none (1 GPU)"},
+        "roofline": leg["roofline"],
+    }
+    if decode is not None:
+        out["decode"] = {"workload": DECODE, "value": round(decode["value"], 1), "unit": "GB/s",
+                         "ms_per_step": round(decode["total_ms"] / args.steps, 4),
+                         "frac_of_hbm_peak": round(decode["value"] / PEAK_HBM_GBS, 4),
+                         "roofline": decode["roofline"]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,7 +34,8 @@ int validate_fwd(const fa_fwd_args &a, FwdParams &p) {
     if (q_nonempty && (!a.q || !a.o)) return FA_ERR_INVALID_ARG;
     if (kv_nonempty && (!a.k || !a.v)) return FA_ERR_INVALID_ARG;
     if (!supported_d(a.d)) return FA_ERR_UNSUPPORTED;
-    if (a.H / a.Hkv > 0x7fffffff || a.Nq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    // Per-head element offsets are 32-bit inside the kernels.
+    if (a.Nq * a.d > 0x7fffffff || a.Nk * a.d > 0x7fffffff) return FA_ERR_UNSUPPORTED;
 
     memset(&p, 0, sizeof p);
     p.q = a.q;

@@ -13,7 +13,8 @@
 //   * scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T
 //     kept in registers), so the 32x32 accumulator gives every lane ONE
 //     query row and 16 of its keys; the partner lane (lane ^ 32) holds the
-//     other 16.  Row max / row sum are in-lane reductions plus one swap.
+//     other 16.  Row max / row sum are in-lane reductions plus one
+//     v_permlane32_swap.
 //   * the output is accumulated transposed, O^T += V^T P^T: the score
 //     accumulator registers, rounded to bf16, are exactly the B operand
 //     (keys permuted consistently with the V^T read), and each lane again
@@ -25,6 +26,17 @@
 //     tile is computed.
 //   * blocks are ordered so that all query tiles of one K/V head run back to
 //     back on the same XCD (shared L2), the longest causal tiles first.
+//
+// Softmax bookkeeping per tile is kept small, since at d = 128 its vector
+// work rivals the matrix work:
+//   * tiles that every row of the block sees in full skip all masking;
+//   * without a soft-cap the row maximum is taken on the raw scores and the
+//     weight is exp2(fma(s, scale*log2 e, -m)): one FMA and one exp each;
+//   * the running maximum is only moved when a tile's maximum exceeds it by
+//     more than TAU (log2 units).  Any reference point gives the same exact
+//     result (the merge rule rescales consistently); this one keeps the
+//     weights <= 2^TAU and makes the rescale of the output, a multiply of
+//     every accumulator, rare.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -32,9 +44,10 @@ namespace fa {
 
 namespace {
 
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup
+constexpr int BM = 128;      // query rows per workgroup
+constexpr int BN = 64;       // keys per tile
+constexpr int NT = 256;      // threads per workgroup
+constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
 
 template <int D>
 struct Smem {
@@ -57,6 +70,23 @@ __device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
     return (a >> 16) | (b & 0xffff0000u);
+}
+
+// {own, partner} values of a lane and lane ^ 32, in either order.
+__device__ __forceinline__ void halves(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_max(float x) {
+    float a, b;
+    halves(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float row_sum(float x) {
+    float a, b;
+    halves(x, a, b);
+    return a + b;
 }
 
 // Block index -> (query tile, head, batch, split).  The unit of locality is
@@ -91,7 +121,95 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
     return w;
 }
 
-template <int D, bool SPLIT>
+// Online-softmax update for one 64-key tile and O^T += V^T P^T.
+// sacc: raw scores q.k (S^T accumulator layout).  lo/hi: this lane's visible
+// keys as offsets from the tile start, applied when `masked`.
+// EXPLICIT: the transformed score t = cap(s*scale)*log2 e (or s*scale*log2 e
+// for a non-positive scale) is formed per element; otherwise the row
+// maximum is taken on raw scores (scale > 0) and t is folded into the FMA
+// that feeds the exp.
+template <int D, bool EXPLICIT, bool CAP>
+__device__ __forceinline__ void tile_update(f32x16 (&sacc)[2], float &m, float &l, f32x16 (&oacc)[D / 32],
+                                            const uint16_t *Vs, bool masked, int lo, int hi, int hf, int l32,
+                                            float c_log2, float scale, float softcap) {
+    using L = Smem<D>;
+    if (EXPLICIT) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                sacc[kb][j] = CAP ? softcap_log2(sacc[kb][j] * scale, softcap) : sacc[kb][j] * c_log2;
+    }
+    if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int koff = kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
+                if (koff < lo || koff >= hi) sacc[kb][j] = kNegInf;
+            }
+    }
+    float mt = sacc[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[kb][j]);
+    if (!EXPLICIT) mt *= c_log2;
+    mt = row_max(mt);
+
+    // Move the reference maximum only when it grew by more than TAU (any lane).
+    if (__builtin_amdgcn_ballot_w64(mt > m + TAU) != 0) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        m = m_new;
+    }
+    const float m_use = m == kNegInf ? 0.0f : m;
+
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float pj = EXPLICIT ? fast_exp2(sacc[kb][j] - m_use) : fast_exp2(fmaf(sacc[kb][j], c_log2, -m_use));
+            sacc[kb][j] = pj;
+            rs += pj;
+        }
+    l += row_sum(rs);
+
+    // O^T += V^T P^T.  k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16):
+    // this lane half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
+    // exactly accumulator elements 8*gp .. 8*gp+7.
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+            u32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] = pack_bf16x2(sacc[kb][8 * gp + 2 * e], sacc[kb][8 * gp + 2 * e + 1]);
+            pf[kb * 2 + gp] = __builtin_bit_cast(bf16x8, x);
+        }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const uint16_t *vrow = Vs + (db * 32 + l32) * L::VSTR + 4 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x2 a0 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16);
+            const u32x2 a1 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16 + 8);
+            const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[ks], oacc[db], 0,
+                                                               0, 0);
+        }
+    }
+}
+
+template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
 __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, const int n_qtiles) {
     using L = Smem<D>;
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::STAGE];
@@ -124,14 +242,16 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
     const int64_t full_lo = lo_last > r_lo ? lo_last : r_lo;
     const int64_t full_hi = hi_first < r_hi ? hi_first : r_hi;
 
-    // This lane's query row and its own visible interval.
+    // This lane's query row and its own visible interval, relative to kbeg.
     const int64_t qrow = q0 + wave * 32 + l32;
-    int64_t kmin, kmax;
+    int lo_rel, hi_rel;
     {
         int64_t lo, hi;
         key_bounds(qrow + off, Nk, p.causal, W, lo, hi);
-        kmin = lo > r_lo ? lo : r_lo;
-        kmax = hi < r_hi ? hi : r_hi;
+        lo = (lo > r_lo ? lo : r_lo) - kbeg;
+        hi = (hi < r_hi ? hi : r_hi) - kbeg;
+        lo_rel = (int)(lo < -1 ? -1 : (lo > 0x3fffffff ? 0x3fffffff : lo));
+        hi_rel = (int)(hi < -1 ? -1 : (hi > 0x3fffffff ? 0x3fffffff : hi));
     }
 
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.H + h) * Nq * D;
@@ -147,9 +267,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
         qf[ds] = __builtin_bit_cast(bf16x8, x);
     }
 
-    // Scores in base 2: t = s * log2(e).
     const float c_log2 = p.scale * kLog2e;
-    const bool capped = p.softcap > 0.0f;
 
     float m = kNegInf, l = 0.0f;
     f32x16 oacc[D / 32];
@@ -159,24 +277,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
         for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
 
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
+    const int kmax_row = (int)Nk - 1;  // keys past the end are clamped (and masked)
 
     u32x4 kreg[L::KCH];
     u32x4 vreg[4];
     const int vkg = tid & 15, vdc = tid >> 4;  // V unit: keys 4*vkg.., dims 8*vdc..
 
-    auto gload = [&](int64_t kt) {
+    auto gload = [&](int kt) {  // kt: first key of the tile (< Nk)
 #pragma unroll
         for (int c = 0; c < L::KCH; ++c) {
             const int chunk = tid + NT * c;
-            const int64_t key = kt + chunk / (D / 8);
-            const int dc = chunk % (D / 8);
-            kreg[c] = key < Nk ? ldg16(K + key * D + dc * 8) : u32x4{0u, 0u, 0u, 0u};
+            const int key = min(kt + chunk / (D / 8), kmax_row);
+            kreg[c] = ldg16(K + key * D + (chunk % (D / 8)) * 8);
         }
         if (tid < L::VUNITS) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t key = kt + vkg * 4 + r;
-                vreg[r] = key < Nk ? ldg16(V + key * D + vdc * 8) : u32x4{0u, 0u, 0u, 0u};
+                const int key = min(kt + vkg * 4 + r, kmax_row);
+                vreg[r] = ldg16(V + key * D + vdc * 8);
             }
         }
     };
@@ -200,13 +318,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
     };
 
     if (ntiles > 0) {
-        gload(kbeg);
+        gload((int)kbeg);
         lstore(0);
         __syncthreads();
     }
 
     for (int it = 0; it < ntiles; ++it) {
-        const int64_t kt = kbeg + (int64_t)it * BN;
+        const int kt = (int)kbeg + it * BN;
         const int buf = it & 1;
         if (it + 1 < ntiles) gload(kt + BN);
 
@@ -227,78 +345,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
             }
         }
 
-        // ---- scale / soft-cap, then mask (after the cap) where needed.
-        // Element j of block kb holds key kt + kb*32 + 8*(j/4) + 4*hf + (j%4).
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                sacc[kb][j] = capped ? softcap_log2(sacc[kb][j] * p.scale, p.softcap) : sacc[kb][j] * c_log2;
-
-        const bool need_mask = !(kt >= full_lo && kt + BN <= full_hi);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int64_t key = kt + kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
-                    if (key < kmin || key >= kmax) sacc[kb][j] = kNegInf;
-                }
-        }
-
-        // ---- online softmax: row max over the 64 keys (this lane's 32 + partner's 32)
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == kNegInf ? 0.0f : m_new;  // no (-inf) - (-inf)
-        const float alpha = fast_exp2(m - m_use);
-        float rs = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float pj = fast_exp2(sacc[kb][j] - m_use);
-                sacc[kb][j] = pj;
-                rs += pj;
-            }
-        rs += __shfl_xor(rs, 32);
-        l = l * alpha + rs;
-        m = m_new;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-
-        // ---- O^T += V^T P^T.  k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16):
-        // this lane half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
-        // exactly accumulator elements 8*gp .. 8*gp+7.
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int gp = 0; gp < 2; ++gp) {
-                u32x4 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    x[e] = pack_bf16x2(sacc[kb][8 * gp + 2 * e], sacc[kb][8 * gp + 2 * e + 1]);
-                pf[kb * 2 + gp] = __builtin_bit_cast(bf16x8, x);
-            }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const uint16_t *vrow = Vs + (db * 32 + l32) * L::VSTR + 4 * hf;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const u32x2 a0 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16);
-                const u32x2 a1 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16 + 8);
-                const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[ks],
-                                                                   oacc[db], 0, 0, 0);
-            }
-        }
+        const bool full = (int64_t)kt >= full_lo && (int64_t)kt + BN <= full_hi;
+        const int lo_t = lo_rel - it * BN, hi_t = hi_rel - it * BN;
+        tile_update<D, EXPLICIT, CAP>(sacc, m, l, oacc, Vs, !full, lo_t, hi_t, hf, l32, c_log2, p.scale,
+                                      p.softcap);
 
         if (it + 1 < ntiles) lstore(buf ^ 1);
         __syncthreads();
@@ -337,23 +387,36 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
     }
 }
 
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
 int launch_one(const FwdParams &p, hipStream_t stream) {
     const int n_qtiles = (int)((p.Nq + BM - 1) / BM);
     const int64_t blocks = p.B * p.H * (int64_t)n_qtiles * p.num_splits;
     if (blocks <= 0) return FA_OK;
     if (blocks > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, SPLIT>), dim3((unsigned)blocks), dim3(NT), 0, stream, p, n_qtiles);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, SPLIT, EXPLICIT, CAP>), dim3((unsigned)blocks), dim3(NT), 0, stream, p,
+                       n_qtiles);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+template <int D, bool SPLIT>
+int launch_s(const FwdParams &p, hipStream_t stream) {
+    if (p.softcap > 0.0f) return launch_one<D, SPLIT, true, true>(p, stream);
+    if (!(p.scale > 0.0f)) return launch_one<D, SPLIT, true, false>(p, stream);
+    return launch_one<D, SPLIT, false, false>(p, stream);
+}
+
+template <int D>
+int launch_d(const FwdParams &p, bool split, hipStream_t stream) {
+    return split ? launch_s<D, true>(p, stream) : launch_s<D, false>(p, stream);
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const FwdParams &p, int d, bool split, hipStream_t stream) {
     switch (d) {
-        case 32: return split ? launch_one<32, true>(p, stream) : launch_one<32, false>(p, stream);
-        case 64: return split ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
-        case 128: return split ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+        case 32: return launch_d<32>(p, split, stream);
+        case 64: return launch_d<64>(p, split, stream);
+        case 128: return launch_d<128>(p, split, stream);
         default: return FA_ERR_UNSUPPORTED;
     }
 }
