@@ -20,10 +20,13 @@
 //     (keys permuted consistently with the V^T read), and each lane again
 //     owns one query row, so the rescale by exp(m_old - m_new) is a per-lane
 //     multiply.
-//   * K is staged row-major and V transposed (key-contiguous) in LDS, both
-//     padded so the MFMA operand reads are bank-conflict free; two LDS
-//     stages: the next tile's global loads are in flight while the current
-//     tile is computed.
+//   * K and V tiles go from HBM straight into LDS (global_load_lds, 16 B per
+//     lane, no register staging), row-major with an XOR swizzle of the
+//     16-byte chunks chosen so that the K operand reads (ds_read_b128) and
+//     the transposing V reads (ds_read_b64_tr_b16, which hand each lane
+//     four keys of one column: the V^T operand) are bank-conflict free.
+//     Two LDS stages in separate arrays: the next tile's loads are in flight
+//     while the current tile is computed.
 //   * blocks are ordered so that all query tiles of one K/V head run back to
 //     back on the same XCD (shared L2), the longest causal tiles first.
 //
@@ -51,26 +54,23 @@ constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
 
 template <int D>
 struct Smem {
-    static constexpr int KSTR = D + 8;   // bf16 per K row in LDS (16 B pad)
-    static constexpr int VSTR = BN + 4;  // bf16 per V^T row in LDS (8 B pad)
-    static constexpr int KTILE = BN * KSTR;
-    static constexpr int VTILE = D * VSTR;
-    static constexpr int STAGE = KTILE + VTILE;
-    static constexpr int KCH = BN * D / 8 / NT;   // 16-B K chunks per thread
-    static constexpr int VUNITS = (BN / 4) * (D / 8);  // 4 keys x 8 dims units
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
+    static constexpr int LPW = BN * CPR / 64 / 4;  // wave load instructions per tile
+    // Swizzled chunk slot of chunk c in row r.  K: c ^ (r % CPR) makes 16
+    // consecutive rows' same chunk hit distinct banks; V: c ^ (2r % CPR)
+    // does the same for the 4-row x 32-byte footprint of a transposing read.
+    __device__ static int kslot(int r, int c) { return c ^ (r % CPR); }
+    __device__ static int vslot(int r, int c) { return c ^ ((2 * r) % CPR); }
 };
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-// Pick two bf16 halves: (lo half of a, lo half of b) or (hi of a, hi of b).
-__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
-    return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // {own, partner} values of a lane and lane ^ 32, in either order.
 __device__ __forceinline__ void halves(float x, float &a, float &b) {
@@ -130,8 +130,8 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
 // that feeds the exp.
 template <int D, bool EXPLICIT, bool CAP>
 __device__ __forceinline__ void tile_update(f32x16 (&sacc)[2], float &m, float &l, f32x16 (&oacc)[D / 32],
-                                            const uint16_t *Vs, bool masked, int lo, int hi, int hf, int l32,
-                                            float c_log2, float scale, float softcap) {
+                                            const char *Vsb, const int (&voff)[D / 32], bool masked, int lo, int hi,
+                                            int hf, float c_log2, float scale, float softcap) {
     using L = Smem<D>;
     if (EXPLICIT) {
 #pragma unroll
@@ -195,16 +195,17 @@ __device__ __forceinline__ void tile_update(f32x16 (&sacc)[2], float &m, float &
                 x[e] = pack_bf16x2(sacc[kb][8 * gp + 2 * e], sacc[kb][8 * gp + 2 * e + 1]);
             pf[kb * 2 + gp] = __builtin_bit_cast(bf16x8, x);
         }
+    // V^T operand: two transposing reads give this lane the keys
+    // +4*hf+[0,4) and +8+4*hf+[0,4) of k-step ks at its column db*32 + lane%32.
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-        const uint16_t *vrow = Vs + (db * 32 + l32) * L::VSTR + 4 * hf;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const u32x2 a0 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16);
-            const u32x2 a1 = *reinterpret_cast<const u32x2 *>(vrow + ks * 16 + 8);
-            const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[ks], oacc[db], 0,
-                                                               0, 0);
+            const char *base = Vsb + voff[db] + ks * 16 * L::CPR * 16;
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 8 * L::CPR * 16));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[db], 0, 0, 0);
         }
     }
 }
@@ -212,9 +213,13 @@ __device__ __forceinline__ void tile_update(f32x16 (&sacc)[2], float &m, float &
 template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
 __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, const int n_qtiles) {
     using L = Smem<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::STAGE];
+    // Two stages, each K tile then V tile; separate arrays so the compiler
+    // can tell the stage being filled from the stage being read.
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[2 * L::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[2 * L::TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const Work w = decode_block(p, n_qtiles);
     const int h = w.h, b = w.b;
@@ -279,58 +284,51 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
     const int kmax_row = (int)Nk - 1;  // keys past the end are clamped (and masked)
 
-    u32x4 kreg[L::KCH];
-    u32x4 vreg[4];
-    const int vkg = tid & 15, vdc = tid >> 4;  // V unit: keys 4*vkg.., dims 8*vdc..
-
-    auto gload = [&](int kt) {  // kt: first key of the tile (< Nk)
+    // Global side of the direct loads: load u of this wave fills LDS chunk
+    // slots q*64 + lane (q = wave*LPW + u) of the tile, i.e. row rr, slot sl.
+    int g_row[L::LPW], g_col[L::LPW];
 #pragma unroll
-        for (int c = 0; c < L::KCH; ++c) {
-            const int chunk = tid + NT * c;
-            const int key = min(kt + chunk / (D / 8), kmax_row);
-            kreg[c] = ldg16(K + key * D + (chunk % (D / 8)) * 8);
-        }
-        if (tid < L::VUNITS) {
+    for (int u = 0; u < L::LPW; ++u) {
+        const int pos = (wave * L::LPW + u) * 64 + lane;
+        g_row[u] = pos / L::CPR;
+        g_col[u] = (pos % L::CPR) * 8;  // slot; the chunk it holds is per K / V
+    }
+    // K operand reads: row kb*32 + l32, chunk 2*ds + hf (bytes from the stage).
+    int koff[D / 16];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = min(kt + vkg * 4 + r, kmax_row);
-                vreg[r] = ldg16(V + key * D + vdc * 8);
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-        uint16_t *Ks = lds + buf * L::STAGE;
-        uint16_t *Vs = Ks + L::KTILE;
+    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = (l32 * L::CPR + L::kslot(l32, 2 * ds + hf)) * 16;
+    // V^T operand reads (see tile_update): row 4*(hf) + e (+ 16*ks, + 8),
+    // column db*32 + 16*(gq%2) + 4*j.
+    int voff[D / 32];
+    {
+        const int gq = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
+        const int row = 4 * (gq >> 1) + e;
 #pragma unroll
-        for (int c = 0; c < L::KCH; ++c) {
-            const int chunk = tid + NT * c;
-            *reinterpret_cast<u32x4 *>(Ks + (chunk / (D / 8)) * L::KSTR + (chunk % (D / 8)) * 8) = kreg[c];
+        for (int db = 0; db < D / 32; ++db) {
+            const int c = db * 4 + 2 * (gq & 1) + (j >> 1);
+            voff[db] = L::TILE * 2 + (row * L::CPR + L::vslot(row, c)) * 16 + (j & 1) * 8;
         }
-        if (tid < L::VUNITS) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {  // dword e of each row: dims 2e, 2e+1
-                u32x2 lo = {pick_lo(vreg[0][e], vreg[1][e]), pick_lo(vreg[2][e], vreg[3][e])};
-                u32x2 hi = {pick_hi(vreg[0][e], vreg[1][e]), pick_hi(vreg[2][e], vreg[3][e])};
-                *reinterpret_cast<u32x2 *>(Vs + (vdc * 8 + 2 * e) * L::VSTR + vkg * 4) = lo;
-                *reinterpret_cast<u32x2 *>(Vs + (vdc * 8 + 2 * e + 1) * L::VSTR + vkg * 4) = hi;
-            }
-        }
-    };
-
-    if (ntiles > 0) {
-        gload((int)kbeg);
-        lstore(0);
-        __syncthreads();
     }
 
-    for (int it = 0; it < ntiles; ++it) {
+    auto issue_loads = [&](int kt, uint16_t *stage) {
+        const bool clamp = kt + BN > (int)Nk;
+#pragma unroll
+        for (int u = 0; u < L::LPW; ++u) {
+            int key = kt + g_row[u];
+            if (clamp) key = min(key, kmax_row);
+            const int rr = g_row[u];
+            const int kc = L::kslot(rr, g_col[u] / 8) * 8;  // chunk held by this slot (xor is an involution)
+            const int vc = L::vslot(rr, g_col[u] / 8) * 8;
+            lds_void *kdst = (lds_void *)(stage + (wave * L::LPW + u) * 64 * 8);
+            lds_void *vdst = (lds_void *)(stage + L::TILE + (wave * L::LPW + u) * 64 * 8);
+            __builtin_amdgcn_global_load_lds((const void *)(K + key * D + kc), kdst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(V + key * D + vc), vdst, 16, 0, 0);
+        }
+    };
+
+    auto compute_tile = [&](int it, const uint16_t *stage) {
         const int kt = (int)kbeg + it * BN;
-        const int buf = it & 1;
-        if (it + 1 < ntiles) gload(kt + BN);
-
-        const uint16_t *Ks = lds + buf * L::STAGE;
-        const uint16_t *Vs = Ks + L::KTILE;
-
+        const char *Ksb = reinterpret_cast<const char *>(stage);
         // ---- S^T = K Q^T for the 64 keys of this tile (two 32-key blocks)
         f32x16 sacc[2];
 #pragma unroll
@@ -339,18 +337,31 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
             for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
 #pragma unroll
             for (int ds = 0; ds < D / 16; ++ds) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(Ks + (kb * 32 + l32) * L::KSTR + ds * 16 + hf * 8);
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(Ksb + kb * 32 * L::CPR * 16 + koff[ds]);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds],
                                                                    sacc[kb], 0, 0, 0);
             }
         }
-
         const bool full = (int64_t)kt >= full_lo && (int64_t)kt + BN <= full_hi;
-        const int lo_t = lo_rel - it * BN, hi_t = hi_rel - it * BN;
-        tile_update<D, EXPLICIT, CAP>(sacc, m, l, oacc, Vs, !full, lo_t, hi_t, hf, l32, c_log2, p.scale,
-                                      p.softcap);
+        tile_update<D, EXPLICIT, CAP>(sacc, m, l, oacc, Ksb, voff, !full, lo_rel - it * BN, hi_rel - it * BN, hf,
+                                      c_log2, p.scale, p.softcap);
+    };
 
-        if (it + 1 < ntiles) lstore(buf ^ 1);
+    if (ntiles > 0) {
+        issue_loads((int)kbeg, lds0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    // Two tiles per trip so each half names its stages statically.
+    for (int it = 0; it < ntiles; it += 2) {
+        if (it + 1 < ntiles) issue_loads((int)kbeg + (it + 1) * BN, lds1);
+        compute_tile(it, lds0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (it + 1 >= ntiles) break;
+        if (it + 2 < ntiles) issue_loads((int)kbeg + (it + 2) * BN, lds0);
+        compute_tile(it + 1, lds1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
