@@ -72,21 +72,22 @@ def to_device(inp, torch):
 
 
 def time_launches(launch, steps, warmup, torch):
-    """Run warmup + timed launches; per-launch HIP event durations (ms)."""
+    """Warmup, then `steps` back-to-back launches bracketed by one pair of
+    HIP events on the launch stream (no events between launches).  Returns
+    (average ms per launch, total ms, wall seconds)."""
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record()
+    start.record()
+    for _ in range(steps):
         launch()
-        e.record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = [s.elapsed_time(e) for s, e in ev]
-    total = ev[0][0].elapsed_time(ev[-1][1])
-    return durs, total, wall
+    total = start.elapsed_time(end)
+    return total / steps, total, wall
 
 
 def bench_prefill(torch, fa, steps, warmup):
@@ -100,9 +101,8 @@ def bench_prefill(torch, fa, steps, warmup):
     def launch():
         fa.fa_fwd(*args)
 
-    durs, total, wall = time_launches(launch, steps, warmup, torch)
+    avg, total, wall = time_launches(launch, steps, warmup, torch)
     flops = wl.algorithmic_flops(w)
-    avg = float(np.mean(durs))
     achieved = flops / (avg * 1e-3) / 1e12
     traffic = measured_traffic("prefill")
     return w, {
@@ -134,16 +134,15 @@ def bench_decode(torch, fa, steps, warmup):
         split()
         combine()
 
-    durs, total, wall = time_launches(launch, steps, warmup, torch)
+    avg, total, wall = time_launches(launch, steps, warmup, torch)
     # the split kernel alone (the dominant kernel) for the roofline
-    sdurs, _, _ = time_launches(split, steps, 2, torch)
+    avg_split, _, _ = time_launches(split, steps, 2, torch)
     nbytes = wl.algorithmic_bytes(w)
     part_bytes = w.B * w.H * w.Nq * S * (w.d + 2) * 4
     split_bytes = nbytes - part_bytes - (w.B * w.H * w.Nq * (w.d * 2 + 4))  # q, k, v in; partials out
-    avg_split = float(np.mean(sdurs))
     achieved = split_bytes / (avg_split * 1e-3) / 1e9
     return w, {
-        "bytes": nbytes, "avg_ms": float(np.mean(durs)), "total_ms": total, "wall_s": wall,
+        "bytes": nbytes, "avg_ms": avg, "total_ms": total, "wall_s": wall,
         "value": nbytes * steps / (total * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),

@@ -62,6 +62,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Reinterpret a 32-bit word as two bf16.  Takes the word by value: applying
+// __builtin_bit_cast directly to an ext_vector element (v[e]) reads element
+// 0 whatever e is with this compiler, so vector elements must pass through a
+// scalar first.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // kappa * tanh(z / kappa) returned in base-2 units (times log2 e).

@@ -8,8 +8,8 @@
 // on chip, and writes the finished output once.  The score matrix never
 // reaches HBM.
 //
-// Tiling on CDNA4:
-//   * workgroup = 4 waves = 128 query rows (32 per wave); key tiles of 64.
+// Tiling on CDNA4: 8 waves per workgroup, two per SIMD, 32 query rows per
+// wave (256 per workgroup), key tiles of 64 shared in LDS by all 8 waves.
 //   * scores are computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T
 //     kept in registers), so the 32x32 accumulator gives every lane ONE
 //     query row and 16 of its keys; the partner lane (lane ^ 32) holds the
@@ -20,13 +20,17 @@
 //     (keys permuted consistently with the V^T read), and each lane again
 //     owns one query row, so the rescale by exp(m_old - m_new) is a per-lane
 //     multiply.
-//   * K and V tiles go from HBM straight into LDS (global_load_lds, 16 B per
-//     lane, no register staging), row-major with an XOR swizzle of the
-//     16-byte chunks chosen so that the K operand reads (ds_read_b128) and
-//     the transposing V reads (ds_read_b64_tr_b16, which hand each lane
-//     four keys of one column: the V^T operand) are bank-conflict free.
-//     Two LDS stages in separate arrays: the next tile's loads are in flight
-//     while the current tile is computed.
+//   * ping-pong: the two waves that share a SIMD alternate between a matrix
+//     phase (scores of tile j and P.V of tile j-1, all MFMA) and a vector
+//     phase (softmax of tile j).  Waves 4..7 run one phase behind waves
+//     0..3, enforced by workgroup barriers, so while one wave of a SIMD
+//     issues MFMAs its partner runs the exp/max/sum work.
+//   * K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16 B
+//     per lane, no register staging; the buffer range check zero-fills rows
+//     past the last key), row-major with an XOR swizzle of the 16-byte
+//     chunks chosen so that the K operand reads (ds_read_b128) and the
+//     transposing V reads (ds_read_b64_tr_b16, which hand each lane four
+//     keys of one column: the V^T operand) are bank-conflict free.
 //   * blocks are ordered so that all query tiles of one K/V head run back to
 //     back on the same XCD (shared L2), the longest causal tiles first.
 //
@@ -47,30 +51,43 @@ namespace fa {
 
 namespace {
 
-constexpr int BM = 128;      // query rows per workgroup
-constexpr int BN = 64;       // keys per tile
-constexpr int NT = 256;      // threads per workgroup
-constexpr float TAU = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr int RB = 1;             // 32-row blocks per wave
+constexpr int NW = 8;             // waves per workgroup (two per SIMD)
+constexpr int BM = NW * 32 * RB;  // query rows per workgroup
+constexpr int BN = 64;            // keys per tile
+constexpr int NT = 64 * NW;       // threads per workgroup
+constexpr int LOADERS = 4;        // waves that issue the tile loads
+constexpr float TAU = 8.0f;       // lazy-rescale threshold, log2 units
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
 struct Smem {
     static constexpr int CPR = D / 8;              // 16-byte chunks per row
     static constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
-    static constexpr int LPW = BN * CPR / 64 / 4;  // wave load instructions per tile
-    // Swizzled chunk slot of chunk c in row r.  K: c ^ (r % CPR) makes 16
-    // consecutive rows' same chunk hit distinct banks; V: c ^ (2r % CPR)
-    // does the same for the 4-row x 32-byte footprint of a transposing read.
+    static constexpr int LPW = BN * CPR / 64 / LOADERS;  // loads per loader wave per tile
+    // Swizzled chunk slot of chunk c in row r.  K: c ^ (r % CPR) puts the
+    // same chunk of 16 consecutive rows in distinct banks.  V: c ^ (4r % CPR)
+    // moves each of the 4 rows a transposing read touches (4 consecutive
+    // rows, 64 bytes each for 32 lanes) to its own 64-byte bank block.
     __device__ static int kslot(int r, int c) { return c ^ (r % CPR); }
-    __device__ static int vslot(int r, int c) { return c ^ ((2 * r) % CPR); }
+    __device__ static int vslot(int r, int c) { return c ^ ((4 * r) % CPR); }
 };
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// 16 bytes per lane from base + voff + soff straight into LDS (dst + 16*lane).
+// The buffer resource bounds the access to [base, base + nbytes): bytes past
+// the end read as zero.  soff is wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(const void *base, int nbytes, lds_void *dst, int voff, int soff) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes,
+                                                                         0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
 
 // {own, partner} values of a lane and lane ^ 32, in either order.
 __device__ __forceinline__ void halves(float x, float &a, float &b) {
@@ -121,105 +138,155 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
     return w;
 }
 
-// Online-softmax update for one 64-key tile and O^T += V^T P^T.
-// sacc: raw scores q.k (S^T accumulator layout).  lo/hi: this lane's visible
-// keys as offsets from the tile start, applied when `masked`.
-// EXPLICIT: the transformed score t = cap(s*scale)*log2 e (or s*scale*log2 e
-// for a non-positive scale) is formed per element; otherwise the row
-// maximum is taken on raw scores (scale > 0) and t is folded into the FMA
-// that feeds the exp.
+// Per-wave state and the pieces of one pipelined step.
 template <int D, bool EXPLICIT, bool CAP>
-__device__ __forceinline__ void tile_update(f32x16 (&sacc)[2], float &m, float &l, f32x16 (&oacc)[D / 32],
-                                            const char *Vsb, const int (&voff)[D / 32], bool masked, int lo, int hi,
-                                            int hf, float c_log2, float scale, float softcap) {
+struct Wave {
     using L = Smem<D>;
-    if (EXPLICIT) {
+    bf16x8 qf[RB][D / 16];      // Q^T operand, per row block
+    f32x16 oacc[RB][D / 32];    // O^T accumulators
+    float m[RB], l[RB];         // lazy reference max (log2 units) and sum
+    float mtrue[RB];            // exact running max (log2 units)
+    int lo_rel[RB], hi_rel[RB]; // visible keys relative to the first tile
+    int koff[D / 16];           // K operand read offsets (bytes)
+    int voff[D / 32];           // V^T operand read offsets (bytes)
+    int hf;
+    float c_log2, scale, softcap;
+
+    // S^T = K Q^T for the 64 keys of a tile, both row blocks.
+    __device__ __forceinline__ void scores(const uint16_t *kbuf, f32x16 (&sacc)[RB][2]) const {
+        const char *Ksb = reinterpret_cast<const char *>(kbuf);
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) sacc[r][kb][j] = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                sacc[kb][j] = CAP ? softcap_log2(sacc[kb][j] * scale, softcap) : sacc[kb][j] * c_log2;
-    }
-    if (masked) {
+            for (int ds = 0; ds < D / 16; ++ds) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(Ksb + kb * 32 * L::CPR * 16 + koff[ds]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int koff = kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
-                if (koff < lo || koff >= hi) sacc[kb][j] = kNegInf;
+                for (int r = 0; r < RB; ++r)
+                    sacc[r][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                          qf[r][ds], sacc[r][kb], 0, 0, 0);
             }
     }
-    float mt = sacc[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, sacc[kb][j]);
-    if (!EXPLICIT) mt *= c_log2;
-    mt = row_max(mt);
 
-    // Move the reference maximum only when it grew by more than TAU (any lane).
-    if (__builtin_amdgcn_ballot_w64(mt > m + TAU) != 0) {
-        const float m_new = fmaxf(m, mt);
-        const float alpha = fast_exp2(m - (m_new == kNegInf ? 0.0f : m_new));
-        l *= alpha;
+    // Online softmax of one tile: masks (if MASK), row max, lazy move of the
+    // reference maximum (branch-free; returns whether any row moved and the
+    // factors), weights rounded to bf16 as the P^T operand.
+    template <bool MASK>
+    __device__ __forceinline__ bool softmax(f32x16 (&sacc)[RB][2], int it, bf16x8 (&pf)[RB][4],
+                                            float (&alpha)[RB]) {
+        float mt[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (EXPLICIT) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        sacc[r][kb][j] = CAP ? softcap_log2(sacc[r][kb][j] * scale, softcap) : sacc[r][kb][j] * c_log2;
+            }
+            if (MASK) {
+                const int lo = lo_rel[r] - it * BN, hi = hi_rel[r] - it * BN;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int ko = kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
+                        if (ko < lo || ko >= hi) sacc[r][kb][j] = kNegInf;
+                    }
+            }
+            float x = sacc[r][0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) x = fmaxf(x, sacc[r][kb][j]);
+            mt[r] = EXPLICIT ? x : x * c_log2;
+            mt[r] = row_max(mt[r]);
+            mtrue[r] = fmaxf(mtrue[r], mt[r]);
+        }
+        bool grow = false;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) grow = grow || (mt[r] > m[r] + TAU);
+        const bool move = __builtin_amdgcn_ballot_w64(grow) != 0;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const float m_new = move ? fmaxf(m[r], mt[r]) : m[r];
+            const float m_use = m_new == kNegInf ? 0.0f : m_new;
+            alpha[r] = fast_exp2(m[r] - m_use);
+            m[r] = m_new;
+            float rs = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float pj = EXPLICIT ? fast_exp2(sacc[r][kb][j] - m_use)
+                                              : fast_exp2(fmaf(sacc[r][kb][j], c_log2, -m_use));
+                    sacc[r][kb][j] = pj;
+                    rs += pj;
+                }
+            l[r] = l[r] * alpha[r] + row_sum(rs);
+            // k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16): this lane
+            // half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
+            // exactly accumulator elements 8*gp .. 8*gp+7.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int gp = 0; gp < 2; ++gp) {
+                    u32x4 xq;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        xq[e] = pack_bf16x2(sacc[r][kb][8 * gp + 2 * e], sacc[r][kb][8 * gp + 2 * e + 1]);
+                    pf[r][kb * 2 + gp] = __builtin_bit_cast(bf16x8, xq);
+                }
+        }
+        return move;
+    }
+
+    __device__ __forceinline__ void rescale(const float (&alpha)[RB]) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) oacc[r][db][j] *= alpha[r];
+    }
+
+    // O^T += V^T P^T.  Two transposing reads give this lane the keys
+    // +4*hf+[0,4) and +8+4*hf+[0,4) of k-step ks at its column db*32 + lane%32.
+    __device__ __forceinline__ void pv(const uint16_t *vbuf, const bf16x8 (&pf)[RB][4]) {
+        const char *Vsb = reinterpret_cast<const char *>(vbuf);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
-        m = m_new;
+            for (int ks = 0; ks < 4; ++ks) {
+                const char *base = Vsb + voff[db] + ks * 16 * L::CPR * 16;
+                const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
+                const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 8 * L::CPR * 16));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+                    oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r][ks], oacc[r][db], 0, 0, 0);
+            }
     }
-    const float m_use = m == kNegInf ? 0.0f : m;
-
-    float rs = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float pj = EXPLICIT ? fast_exp2(sacc[kb][j] - m_use) : fast_exp2(fmaf(sacc[kb][j], c_log2, -m_use));
-            sacc[kb][j] = pj;
-            rs += pj;
-        }
-    l += row_sum(rs);
-
-    // O^T += V^T P^T.  k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16):
-    // this lane half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
-    // exactly accumulator elements 8*gp .. 8*gp+7.
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-            u32x4 x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x[e] = pack_bf16x2(sacc[kb][8 * gp + 2 * e], sacc[kb][8 * gp + 2 * e + 1]);
-            pf[kb * 2 + gp] = __builtin_bit_cast(bf16x8, x);
-        }
-    // V^T operand: two transposing reads give this lane the keys
-    // +4*hf+[0,4) and +8+4*hf+[0,4) of k-step ks at its column db*32 + lane%32.
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const char *base = Vsb + voff[db] + ks * 16 * L::CPR * 16;
-            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
-            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 8 * L::CPR * 16));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ks], oacc[db], 0, 0, 0);
-        }
-    }
-}
+};
 
 template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
-__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, const int n_qtiles) {
+__global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, const int n_qtiles) {
     using L = Smem<D>;
-    // Two stages, each K tile then V tile; separate arrays so the compiler
-    // can tell the stage being filled from the stage being read.
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[2 * L::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[2 * L::TILE];
+    // Separate arrays per buffer so the compiler can tell the buffer being
+    // filled from the buffers being read.
+    __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t kbuf1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[L::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool leader = wave < LOADERS;  // waves 0..3 lead and load; 4..7 trail
     const int l32 = lane & 31, hf = lane >> 5;
     const Work w = decode_block(p, n_qtiles);
     const int h = w.h, b = w.b;
@@ -247,127 +314,130 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
     const int64_t full_lo = lo_last > r_lo ? lo_last : r_lo;
     const int64_t full_hi = hi_first < r_hi ? hi_first : r_hi;
 
-    // This lane's query row and its own visible interval, relative to kbeg.
-    const int64_t qrow = q0 + wave * 32 + l32;
-    int lo_rel, hi_rel;
-    {
-        int64_t lo, hi;
-        key_bounds(qrow + off, Nk, p.causal, W, lo, hi);
-        lo = (lo > r_lo ? lo : r_lo) - kbeg;
-        hi = (hi < r_hi ? hi : r_hi) - kbeg;
-        lo_rel = (int)(lo < -1 ? -1 : (lo > 0x3fffffff ? 0x3fffffff : lo));
-        hi_rel = (int)(hi < -1 ? -1 : (hi > 0x3fffffff ? 0x3fffffff : hi));
-    }
-
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.H + h) * Nq * D;
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * Nk * D;
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * Nk * D;
 
-    // Q^T fragments (the B operand of S^T = K Q^T): row qrow, 8 dims per step.
-    bf16x8 qf[D / 16];
+    Wave<D, EXPLICIT, CAP> st;
+    st.hf = hf;
+    st.c_log2 = p.scale * kLog2e;
+    st.scale = p.scale;
+    st.softcap = p.softcap;
+    const int64_t qrow = q0 + wave * 32 + l32;
+    {
+        // This lane's query row and its visible interval, relative to kbeg.
+        int64_t lo, hi;
+        key_bounds(qrow + off, Nk, p.causal, W, lo, hi);
+        lo = (lo > r_lo ? lo : r_lo) - kbeg;
+        hi = (hi < r_hi ? hi : r_hi) - kbeg;
+        st.lo_rel[0] = (int)(lo < -1 ? -1 : (lo > 0x3fffffff ? 0x3fffffff : lo));
+        st.hi_rel[0] = (int)(hi < -1 ? -1 : (hi > 0x3fffffff ? 0x3fffffff : hi));
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (qrow < Nq) x = ldg16(Q + qrow * D + ds * 16 + hf * 8);
-        qf[ds] = __builtin_bit_cast(bf16x8, x);
+        for (int ds = 0; ds < D / 16; ++ds) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (qrow < Nq) x = ldg16(Q + qrow * D + ds * 16 + hf * 8);
+            st.qf[0][ds] = __builtin_bit_cast(bf16x8, x);
+        }
+        st.m[0] = kNegInf;
+        st.mtrue[0] = kNegInf;
+        st.l[0] = 0.0f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) st.oacc[0][db][j] = 0.0f;
     }
-
-    const float c_log2 = p.scale * kLog2e;
-
-    float m = kNegInf, l = 0.0f;
-    f32x16 oacc[D / 32];
+    // K operand reads: row kb*32 + l32, chunk 2*ds + hf.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.0f;
-
-    const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
-    const int kmax_row = (int)Nk - 1;  // keys past the end are clamped (and masked)
-
-    // Global side of the direct loads: load u of this wave fills LDS chunk
-    // slots q*64 + lane (q = wave*LPW + u) of the tile, i.e. row rr, slot sl.
-    int g_row[L::LPW], g_col[L::LPW];
-#pragma unroll
-    for (int u = 0; u < L::LPW; ++u) {
-        const int pos = (wave * L::LPW + u) * 64 + lane;
-        g_row[u] = pos / L::CPR;
-        g_col[u] = (pos % L::CPR) * 8;  // slot; the chunk it holds is per K / V
-    }
-    // K operand reads: row kb*32 + l32, chunk 2*ds + hf (bytes from the stage).
-    int koff[D / 16];
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) koff[ds] = (l32 * L::CPR + L::kslot(l32, 2 * ds + hf)) * 16;
-    // V^T operand reads (see tile_update): row 4*(hf) + e (+ 16*ks, + 8),
-    // column db*32 + 16*(gq%2) + 4*j.
-    int voff[D / 32];
+    for (int ds = 0; ds < D / 16; ++ds) st.koff[ds] = (l32 * L::CPR + L::kslot(l32, 2 * ds + hf)) * 16;
+    // V^T operand reads: lane in group gq = lane/16 provides row 4*(gq/2) + e
+    // (e = (lane%16)/4; + 16*ks, + 8 for the second read) and column
+    // db*32 + 16*(gq%2) + 4*j (j = lane%4).
     {
         const int gq = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
         const int row = 4 * (gq >> 1) + e;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const int c = db * 4 + 2 * (gq & 1) + (j >> 1);
-            voff[db] = L::TILE * 2 + (row * L::CPR + L::vslot(row, c)) * 16 + (j & 1) * 8;
+            st.voff[db] = (row * L::CPR + L::vslot(row, c)) * 16 + (j & 1) * 8;
         }
     }
 
-    auto issue_loads = [&](int kt, uint16_t *stage) {
-        const bool clamp = kt + BN > (int)Nk;
+    // Direct loads (leader waves only): load u of loader wave lw fills LDS
+    // chunk slots q*64 + lane (q = lw*LPW + u) of a tile, i.e. row rr, slot
+    // sl, which holds chunk kslot(rr, sl) of K (vslot for V; xor is its own
+    // inverse).
+    const int lw = leader ? wave : 0;
+    int k_goff[L::LPW], v_goff[L::LPW];
 #pragma unroll
-        for (int u = 0; u < L::LPW; ++u) {
-            int key = kt + g_row[u];
-            if (clamp) key = min(key, kmax_row);
-            const int rr = g_row[u];
-            const int kc = L::kslot(rr, g_col[u] / 8) * 8;  // chunk held by this slot (xor is an involution)
-            const int vc = L::vslot(rr, g_col[u] / 8) * 8;
-            lds_void *kdst = (lds_void *)(stage + (wave * L::LPW + u) * 64 * 8);
-            lds_void *vdst = (lds_void *)(stage + L::TILE + (wave * L::LPW + u) * 64 * 8);
-            __builtin_amdgcn_global_load_lds((const void *)(K + key * D + kc), kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(V + key * D + vc), vdst, 16, 0, 0);
-        }
+    for (int u = 0; u < L::LPW; ++u) {
+        const int pos = (lw * L::LPW + u) * 64 + lane;
+        const int rr = pos / L::CPR, sl = pos % L::CPR;
+        k_goff[u] = (rr * D + L::kslot(rr, sl) * 8) * 2;
+        v_goff[u] = (rr * D + L::vslot(rr, sl) * 8) * 2;
+    }
+    const int head_bytes = (int)(Nk * D * 2);
+    const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
+    const int kt0 = (int)kbeg;
+
+    auto load_k = [&](int t, uint16_t *buf) {
+        const int toff = (kt0 + t * BN) * D * 2;
+#pragma unroll
+        for (int u = 0; u < L::LPW; ++u)
+            buffer_load_lds16(K, head_bytes, (lds_void *)(buf + (lw * L::LPW + u) * 64 * 8), k_goff[u], toff);
+    };
+    auto load_v = [&](int t, uint16_t *buf) {
+        const int toff = (kt0 + t * BN) * D * 2;
+#pragma unroll
+        for (int u = 0; u < L::LPW; ++u)
+            buffer_load_lds16(V, head_bytes, (lds_void *)(buf + (lw * L::LPW + u) * 64 * 8), v_goff[u], toff);
+    };
+    auto is_full = [&](int t) {
+        const int64_t kt = kbeg + (int64_t)t * BN;
+        return kt >= full_lo && kt + BN <= full_hi;
     };
 
-    auto compute_tile = [&](int it, const uint16_t *stage) {
-        const int kt = (int)kbeg + it * BN;
-        const char *Ksb = reinterpret_cast<const char *>(stage);
-        // ---- S^T = K Q^T for the 64 keys of this tile (two 32-key blocks)
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.0f;
-#pragma unroll
-            for (int ds = 0; ds < D / 16; ++ds) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(Ksb + kb * 32 * L::CPR * 16 + koff[ds]);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds],
-                                                                   sacc[kb], 0, 0, 0);
-            }
+    f32x16 sacc[RB][2];
+    bf16x8 pf[RB][4];
+    // Step j: matrix phase (loads for tiles j+1 / j by the leaders, scores of
+    // tile j from kcur, P.V of tile j-1 from vprev), barrier, vector phase
+    // (softmax of tile j), barrier.  kload/vload receive K of tile j+1 and V
+    // of tile j.
+    auto step = [&](int j, const uint16_t *kcur, const uint16_t *vprev, uint16_t *kload, uint16_t *vload) {
+        if (leader) {
+            if (j + 1 < ntiles) load_k(j + 1, kload);
+            if (j < ntiles) load_v(j, vload);
         }
-        const bool full = (int64_t)kt >= full_lo && (int64_t)kt + BN <= full_hi;
-        tile_update<D, EXPLICIT, CAP>(sacc, m, l, oacc, Ksb, voff, !full, lo_rel - it * BN, hi_rel - it * BN, hf,
-                                      c_log2, p.scale, p.softcap);
+        if (j < ntiles) st.scores(kcur, sacc);
+        if (j >= 1) st.pv(vprev, pf);
+        __syncthreads();
+        if (j < ntiles) {
+            float alpha[RB];
+            const bool move = is_full(j) ? st.template softmax<false>(sacc, j, pf, alpha)
+                                         : st.template softmax<true>(sacc, j, pf, alpha);
+            if (move) st.rescale(alpha);
+        }
+        if (leader) __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     };
 
-    if (ntiles > 0) {
-        issue_loads((int)kbeg, lds0);
+    if (leader && ntiles > 0) {
+        load_k(0, kbuf0);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
     }
-    // Two tiles per trip so each half names its stages statically.
-    for (int it = 0; it < ntiles; it += 2) {
-        if (it + 1 < ntiles) issue_loads((int)kbeg + (it + 1) * BN, lds1);
-        compute_tile(it, lds0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (it + 1 >= ntiles) break;
-        if (it + 2 < ntiles) issue_loads((int)kbeg + (it + 2) * BN, lds0);
-        compute_tile(it + 1, lds1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    __syncthreads();
+    if (!leader) __syncthreads();  // trail the leaders by one phase
+    // Tile j's K sits in kbuf[j % 2], its V in vbuf[j % 2].
+    for (int j = 0; j <= ntiles; j += 2) {
+        step(j, kbuf0, vbuf1, kbuf1, vbuf0);
+        if (j + 1 > ntiles) break;
+        step(j + 1, kbuf1, vbuf0, kbuf0, vbuf1);
     }
+    if (leader) __syncthreads();  // same barrier count for both groups
 
     // ---- epilogue: O = acc / l.  Lane holds dims db*32 + 8*(j/4) + 4*hf + (j%4).
     if (qrow >= Nq) return;
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lr = st.l[0];
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     const int64_t row = ((int64_t)b * p.H + h) * Nq + qrow;
     if (!SPLIT) {
         uint16_t *O = static_cast<uint16_t *>(p.o) + row * D;
@@ -375,11 +445,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                u32x2 x = {pack_bf16x2(oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
+                u32x2 x = {pack_bf16x2(st.oacc[0][db][4 * gq] * inv, st.oacc[0][db][4 * gq + 1] * inv),
+                           pack_bf16x2(st.oacc[0][db][4 * gq + 2] * inv, st.oacc[0][db][4 * gq + 3] * inv)};
                 *reinterpret_cast<u32x2 *>(O + db * 32 + 8 * gq + 4 * hf) = x;
             }
-        if (p.lse && hf == 0) p.lse[row] = l > 0.0f ? (m + __log2f(l)) * kLn2 : kNegInf;
+        if (p.lse && hf == 0) p.lse[row] = lr > 0.0f ? (st.m[0] + __log2f(lr)) * kLn2 : kNegInf;
     } else {
         const int64_t prow = row * p.num_splits + w.split;
         float *Op = p.o_part + prow * D;
@@ -387,13 +457,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(const FwdParams p, cons
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                f32x4 x = {oacc[db][4 * gq] * inv, oacc[db][4 * gq + 1] * inv, oacc[db][4 * gq + 2] * inv,
-                           oacc[db][4 * gq + 3] * inv};
+                f32x4 x = {st.oacc[0][db][4 * gq] * inv, st.oacc[0][db][4 * gq + 1] * inv,
+                           st.oacc[0][db][4 * gq + 2] * inv, st.oacc[0][db][4 * gq + 3] * inv};
                 *reinterpret_cast<f32x4 *>(Op + db * 32 + 8 * gq + 4 * hf) = x;
             }
         if (hf == 0) {
-            p.m_part[prow] = l > 0.0f ? m * kLn2 : kNegInf;
-            p.l_part[prow] = l;
+            // Report the split's exact maximum, with l relative to it.
+            p.m_part[prow] = lr > 0.0f ? st.mtrue[0] * kLn2 : kNegInf;
+            p.l_part[prow] = lr > 0.0f ? lr * fast_exp2(st.m[0] - st.mtrue[0]) : 0.0f;
         }
     }
 }

@@ -14,9 +14,12 @@
 //   * a key row of d bf16 is read by d/8 lanes, 16 bytes each, so one wave
 //     load instruction covers 64*16 = 1 KiB of consecutive keys; each group
 //     of d/8 lanes is an independent online-softmax stream over its keys;
-//   * dot products are VALU FMAs reduced across the d/8 lanes with DPP row
-//     permutes; the streams of the workgroup are merged in LDS at the end
-//     with the same merge rule as fa_combine.
+//   * dot products use v_dot2_f32_bf16 on the raw bf16 pairs (two products,
+//     fp32 accumulation), reduced across the d/8 lanes with DPP row
+//     permutes; P.V pairs two keys held by the same lane so each output
+//     element costs one dot2 per row, with P rounded to bf16 as in the
+//     prefill kernel; the streams of the workgroup are merged in LDS at the
+//     end with the same merge rule as fa_combine.
 #include <math.h>
 
 #include "fa_device.h"
@@ -29,8 +32,6 @@ namespace {
 constexpr int NT = 256;
 constexpr int U = 8;          // key rows per stream per iteration
 constexpr int MAX_ROWS = 4;   // query rows per pass of the decode kernel
-
-__device__ __forceinline__ float dpp_f(float x, int ctrl);
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -48,13 +49,14 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <int D, int R>
+template <int D, int R, bool CAP>
 __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
     constexpr int LPK = D / 8;           // lanes per key row
     constexpr int KPW = 64 / LPK;        // keys (streams) per wave instruction
     constexpr int NSTREAM = 4 * KPW;     // streams per workgroup
     constexpr int KPI = 4 * U * KPW;     // keys per iteration per workgroup
-    __shared__ float Sm[NSTREAM * R], Sl[NSTREAM * R];
+    constexpr float TAU = 8.0f;          // lazy-rescale threshold, log2 units
+    __shared__ float Sm[NSTREAM * R], Sl[NSTREAM * R], St[NSTREAM * R];
     __shared__ __attribute__((aligned(16))) float Sacc[NSTREAM * R * D];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -68,32 +70,31 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
 
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * Nk * D;
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * Nk * D;
-    const bool capped = p.softcap > 0.0f;
+    const float c_log2 = p.scale * kLog2e;
 
     for (int r0 = 0; r0 < GR; r0 += R) {
-        float q[R][8], acc[R][8], m[R], l[R];
+        u32x4 qb[R];              // this lane's 8 dims of each query row, bf16 pairs
+        float acc[R][8], m[R], l[R];
+        float mtrue[R];           // exact running maximum (m is a lazy reference)
         int64_t kmin[R], kmax[R];
         int64_t kb = s_hi, ke = s_lo;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int rr = r0 + r;
             m[r] = kNegInf;
+            mtrue[r] = kNegInf;
             l[r] = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
             kmin[r] = 0;
             kmax[r] = 0;
+            qb[r] = u32x4{0u, 0u, 0u, 0u};
             if (rr < GR) {
                 const int hg = rr / (int)Nq;
                 const int64_t i = rr % Nq;
                 const int h = g * p.group + hg;
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(
-                    static_cast<const uint16_t *>(p.q) + (((int64_t)b * p.H + h) * Nq + i) * D + dl);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    q[r][2 * e] = bf16lo_to_f32(x[e]) * p.scale;
-                    q[r][2 * e + 1] = bf16hi_to_f32(x[e]) * p.scale;
-                }
+                qb[r] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.q) +
+                                                         (((int64_t)b * p.H + h) * Nq + i) * D + dl);
                 int64_t lo, hi;
                 key_bounds(i + off, Nk, p.causal, head_window_of(p, h), lo, hi);
                 kmin[r] = lo > s_lo ? lo : s_lo;
@@ -102,9 +103,6 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
                     kb = kmin[r] < kb ? kmin[r] : kb;
                     ke = kmax[r] > ke ? kmax[r] : ke;
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) q[r][e] = 0.0f;
             }
         }
 
@@ -118,47 +116,64 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
                 kr[u] = in ? *reinterpret_cast<const u32x4 *>(K + key[u] * D + dl) : u32x4{0u, 0u, 0u, 0u};
                 vr[u] = in ? *reinterpret_cast<const u32x4 *>(V + key[u] * D + dl) : u32x4{0u, 0u, 0u, 0u};
             }
-            float s[U][R];
+            // Scores in log2 units: dot2 on bf16 pairs, reduced over the d/8
+            // lanes of the key, scaled (and capped) once.
+            float t[U][R];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float kf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kf[2 * e] = bf16lo_to_f32(kr[u][e]);
-                    kf[2 * e + 1] = bf16hi_to_f32(kr[u][e]);
-                }
+            for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     float d0 = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) d0 = fmaf(q[r][e], kf[e], d0);
+                    for (int e = 0; e < 4; ++e)
+                        d0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qb[r][e]), as_bf16x2(kr[u][e]), d0, false);
                     d0 = group_sum<LPK>(d0);
-                    if (capped) d0 = p.softcap * tanhf(d0 / p.softcap);
-                    s[u][r] = (key[u] >= kmin[r] && key[u] < kmax[r]) ? d0 : kNegInf;
+                    d0 = CAP ? softcap_log2(d0 * p.scale, p.softcap) : d0 * c_log2;
+                    t[u][r] = (key[u] >= kmin[r] && key[u] < kmax[r]) ? d0 : kNegInf;
                 }
-            }
+            // Move each stream's reference maximum only when it grew by more
+            // than TAU (the result is the same for any reference point).
+            float mx[R];
+            bool grow = false;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                float mx = s[0][r];
+                mx[r] = t[0][r];
 #pragma unroll
-                for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][r]);
-                const float m_new = fmaxf(m[r], mx);
-                const float m_use = m_new == kNegInf ? 0.0f : m_new;
-                const float alpha = fast_exp2((m[r] - m_use) * kLog2e);
-                l[r] *= alpha;
+                for (int u = 1; u < U; ++u) mx[r] = fmaxf(mx[r], t[u][r]);
+                mtrue[r] = fmaxf(mtrue[r], mx[r]);
+                grow = grow || (mx[r] > m[r] + TAU);
+            }
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+                for (int r = 0; r < R; ++r) {
+                    const float m_new = fmaxf(m[r], mx[r]);
+                    const float alpha = fast_exp2(m[r] - (m_new == kNegInf ? 0.0f : m_new));
+                    l[r] *= alpha;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const float pu = fast_exp2((s[u][r] - m_use) * kLog2e);
-                    l[r] += pu;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[r][2 * e] = fmaf(pu, bf16lo_to_f32(vr[u][e]), acc[r][2 * e]);
-                        acc[r][2 * e + 1] = fmaf(pu, bf16hi_to_f32(vr[u][e]), acc[r][2 * e + 1]);
-                    }
+                    for (int e = 0; e < 8; ++e) acc[r][e] *= alpha;
+                    m[r] = m_new;
                 }
-                m[r] = m_new;
+            }
+            // P V over key pairs (u, u+1) held by this lane: one dot2 per output
+            // element and row on (V_u[e], V_u+1[e]) . (p_u, p_u+1), p rounded to bf16.
+#pragma unroll
+            for (int u = 0; u < U; u += 2) {
+                uint32_t vp[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vp[2 * e] = (vr[u][e] & 0xffffu) | (vr[u + 1][e] << 16);
+                    vp[2 * e + 1] = (vr[u][e] >> 16) | (vr[u + 1][e] & 0xffff0000u);
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float m_use = m[r] == kNegInf ? 0.0f : m[r];
+                    const float p0 = fast_exp2(t[u][r] - m_use), p1 = fast_exp2(t[u + 1][r] - m_use);
+                    l[r] += p0 + p1;
+                    const bf16x2 pp = as_bf16x2(pack_bf16x2(p0, p1));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[r][e] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(vp[e]), pp, acc[r][e], false);
+                }
             }
         }
 
@@ -168,6 +183,7 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
             if ((lane % LPK) == 0) {
                 Sm[st * R + r] = m[r];
                 Sl[st * R + r] = l[r];
+                St[st * R + r] = mtrue[r];
             }
             float *dst = Sacc + (st * R + r) * D + dl;
             *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
@@ -178,14 +194,17 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
             const int r = idx / D, dd = idx % D;
             const int rr = r0 + r;
             if (rr >= GR) continue;
-            float M = kNegInf;
-            for (int t = 0; t < NSTREAM; ++t) M = fmaxf(M, Sm[t * R + r]);
+            float M = kNegInf, Mt = kNegInf;
+            for (int t2 = 0; t2 < NSTREAM; ++t2) {
+                M = fmaxf(M, Sm[t2 * R + r]);
+                Mt = fmaxf(Mt, St[t2 * R + r]);
+            }
             const float M_use = M == kNegInf ? 0.0f : M;
             float Lsum = 0.0f, O = 0.0f;
-            for (int t = 0; t < NSTREAM; ++t) {
-                const float wgt = fast_exp2((Sm[t * R + r] - M_use) * kLog2e);
-                Lsum = fmaf(wgt, Sl[t * R + r], Lsum);
-                O = fmaf(wgt, Sacc[(t * R + r) * D + dd], O);
+            for (int t2 = 0; t2 < NSTREAM; ++t2) {
+                const float wgt = fast_exp2(Sm[t2 * R + r] - M_use);
+                Lsum = fmaf(wgt, Sl[t2 * R + r], Lsum);
+                O = fmaf(wgt, Sacc[(t2 * R + r) * D + dd], O);
             }
             const int hg = rr / (int)Nq;
             const int64_t i = rr % Nq;
@@ -193,58 +212,108 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
             const int64_t prow = (((int64_t)b * p.H + h) * Nq + i) * p.num_splits + split;
             p.o_part[prow * D + dd] = Lsum > 0.0f ? O / Lsum : 0.0f;
             if (dd == 0) {
-                p.m_part[prow] = Lsum > 0.0f ? M : kNegInf;
-                p.l_part[prow] = Lsum;
+                // Report the split's exact maximum, with l relative to it.
+                p.m_part[prow] = Lsum > 0.0f ? Mt * kLn2 : kNegInf;
+                p.l_part[prow] = Lsum > 0.0f ? Lsum * fast_exp2(M - Mt) : 0.0f;
             }
         }
         __syncthreads();
     }
 }
 
-template <int D>
-int launch_decode_d(const FwdParams &p, hipStream_t stream) {
+template <int D, bool CAP>
+int launch_decode_dc(const FwdParams &p, hipStream_t stream) {
     const int GR = p.group * (int)p.Nq;
     dim3 grid((unsigned)p.num_splits, (unsigned)p.Hkv, (unsigned)p.B);
     if (GR <= 1)
-        hipLaunchKernelGGL((splitkv_decode_kernel<D, 1>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((splitkv_decode_kernel<D, 1, CAP>), grid, dim3(NT), 0, stream, p);
     else if (GR <= 2)
-        hipLaunchKernelGGL((splitkv_decode_kernel<D, 2>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((splitkv_decode_kernel<D, 2, CAP>), grid, dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((splitkv_decode_kernel<D, MAX_ROWS>), grid, dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((splitkv_decode_kernel<D, MAX_ROWS, CAP>), grid, dim3(NT), 0, stream, p);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-// One wave per output row: m = max_s m_s over non-empty splits, weights
-// w_s = exp(m_s - m) l_s, O = sum_s w_s O_s / sum_s w_s, lse = m + ln sum_s w_s.
 template <int D>
-__global__ __launch_bounds__(NT) void combine_kernel(const float *__restrict__ o_part, const float *__restrict__ m_part,
+int launch_decode_d(const FwdParams &p, hipStream_t stream) {
+    return p.softcap > 0.0f ? launch_decode_dc<D, true>(p, stream) : launch_decode_dc<D, false>(p, stream);
+}
+
+// Wave-wide reductions (all 64 lanes receive the result).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// One 64-lane workgroup per output row.  Lanes first take one split each
+// (64 at a time): m = max_s m_s over non-empty splits, weights
+// w_s = exp(m_s - m) l_s, l = sum_s w_s, kept in LDS.  Then each lane
+// accumulates O[d] = sum_s w_s O_s[d] / l for its D/64 columns (or one
+// column for D < 64), with the split loop unrolled so several partial rows
+// are in flight.  lse = m + ln l.
+template <int D>
+__global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ o_part, const float *__restrict__ m_part,
                                                      const float *__restrict__ l_part, void *o, float *lse,
-                                                     const int64_t rows, const int S, const int out_bf16) {
+                                                     const int S, const int out_bf16) {
     constexpr int PER = D >= 64 ? D / 64 : 1;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
-    if (row >= rows) return;
+    constexpr int MAXS = 256;  // splits whose weights stay in LDS; more use several passes
+    __shared__ float wsh[MAXS];
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;
     const float *mr = m_part + row * S;
     const float *lr = l_part + row * S;
+
     float M = kNegInf;
-    for (int s = 0; s < S; ++s)
+    for (int s = lane; s < S; s += 64)
         if (lr[s] > 0.0f) M = fmaxf(M, mr[s]);
+    M = wave_max(M);
+
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
     float Lsum = 0.0f;
     if (M != kNegInf) {
-        for (int s = 0; s < S; ++s) {
-            const float ls = lr[s];
-            if (!(ls > 0.0f)) continue;
-            const float wgt = expf(mr[s] - M) * ls;
-            Lsum += wgt;
-            const float *os = o_part + (row * S + s) * D;
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int dd = lane + 64 * k;
-                if (dd < D) acc[k] = fmaf(wgt, os[dd], acc[k]);
+        for (int s0 = 0; s0 < S; s0 += MAXS) {
+            const int ns = S - s0 < MAXS ? S - s0 : MAXS;
+            float part = 0.0f;
+            for (int s = lane; s < ns; s += 64) {
+                const float ls = lr[s0 + s];
+                const float wgt = ls > 0.0f ? expf(mr[s0 + s] - M) * ls : 0.0f;
+                wsh[s] = wgt;
+                part += wgt;
             }
+            Lsum += wave_sum(part);
+            __syncthreads();
+            const float *os = o_part + (row * S + s0) * D;
+            int s = 0;
+            for (; s + 4 <= ns; s += 4) {
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int dd = lane + 64 * k;
+                    if (dd < D) {
+                        const float x0 = os[(s + 0) * D + dd], x1 = os[(s + 1) * D + dd];
+                        const float x2 = os[(s + 2) * D + dd], x3 = os[(s + 3) * D + dd];
+                        acc[k] = fmaf(wsh[s], x0, acc[k]);
+                        acc[k] = fmaf(wsh[s + 1], x1, acc[k]);
+                        acc[k] = fmaf(wsh[s + 2], x2, acc[k]);
+                        acc[k] = fmaf(wsh[s + 3], x3, acc[k]);
+                    }
+                }
+            }
+            for (; s < ns; ++s) {
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int dd = lane + 64 * k;
+                    if (dd < D) acc[k] = fmaf(wsh[s], os[s * D + dd], acc[k]);
+                }
+            }
+            __syncthreads();
         }
     }
 #pragma unroll
@@ -265,11 +334,10 @@ __global__ __launch_bounds__(NT) void combine_kernel(const float *__restrict__ o
 template <int D>
 int launch_combine_d(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse,
                      int64_t rows, int S, int out_dtype, hipStream_t stream) {
-    const int64_t blocks = (rows + 3) / 4;
-    if (blocks == 0) return FA_OK;
-    if (blocks > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)blocks), dim3(NT), 0, stream, o_part, m_part, l_part, o,
-                       lse, rows, S, out_dtype == FA_DTYPE_BF16 ? 1 : 0);
+    if (rows == 0) return FA_OK;
+    if (rows > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)rows), dim3(64), 0, stream, o_part, m_part, l_part, o, lse,
+                       S, out_dtype == FA_DTYPE_BF16 ? 1 : 0);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

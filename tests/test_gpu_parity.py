@@ -284,10 +284,17 @@ def test_splitkv_matches_unsplit(S, shape):
     print(f"case splitkv S={S} shape={shape}", flush=True)
     inp = rand_inputs(B, H, Hkv, Nq, Nk, d, seed=20 + S, dtype="bf16")
     kw = dict(causal=True, softcap=30.0) if Nq > 1 else {}
-    o, lse, _ = run_split(inp, S, 1.0 / math.sqrt(d), **kw)
+    o, lse, (op, mp, lp) = run_split(inp, S, 1.0 / math.sqrt(d), **kw)
     ref = oracle.attention(inp["q"], inp["k"], inp["v"], 1.0 / math.sqrt(d), **kw)
     check_o(o, ref["o"], "bf16", f"split S={S}")
     check_lse(lse, ref["lse"], "bf16", f"split S={S}")
+    # Each partial is its chunk's own (maximum, sum, normalised output).
+    rop, rmp, rlp = oracle.split_partials(inp["q"], inp["k"], inp["v"], 1.0 / math.sqrt(d), S, **kw)
+    fin = np.isfinite(rmp)
+    assert np.array_equal(fin, np.isfinite(mp)) and np.all(lp[~fin] == 0)
+    assert np.allclose(mp[fin], rmp[fin], rtol=1e-3, atol=1e-3)
+    assert np.allclose(lp[fin], rlp[fin], rtol=2e-3, atol=0)
+    assert np.max(np.abs(op - rop)) < BF16_MAX
 
 
 def test_splitkv_window_and_empty_splits():
