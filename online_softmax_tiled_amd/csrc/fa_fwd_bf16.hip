@@ -28,9 +28,14 @@
 //   * K and V tiles go from HBM straight into LDS (buffer_load ... lds, 16 B
 //     per lane, no register staging; the buffer range check zero-fills rows
 //     past the last key), row-major with an XOR swizzle of the 16-byte
-//     chunks chosen so that the K operand reads (ds_read_b128) and the
-//     transposing V reads (ds_read_b64_tr_b16, which hand each lane four
-//     keys of one column: the V^T operand) are bank-conflict free.
+//     chunks so the K operand reads (ds_read_b128) are bank-conflict free.
+//   * each V tile is transposed once per workgroup: every loading wave
+//     turns the 16 keys it loaded into V^T rows with transposing reads
+//     (ds_read_b64_tr_b16 hands a lane four keys of one column) and 8-byte
+//     writes into a V^T tile whose keys are permuted within each group of 16
+//     (bits 2 and 3 of the key index swapped), so the 8 keys a lane supplies
+//     to one P.V k-step are contiguous and the V^T operand is a single
+//     ds_read_b128 (the transposing read is several times slower per byte).
 //   * blocks are ordered so that all query tiles of one K/V head run back to
 //     back on the same XCD (shared L2), the longest causal tiles first.
 //
@@ -74,6 +79,11 @@ struct Smem {
     // rows, 64 bytes each for 32 lanes) to its own 64-byte bank block.
     __device__ static int kslot(int r, int c) { return c ^ (r % CPR); }
     __device__ static int vslot(int r, int c) { return c ^ ((4 * r) % CPR); }
+    // V^T tile: D rows (one per column of V) of BN = 64 permuted keys, 128
+    // bytes per row; 16-byte chunk c of row d sits in slot c ^ ((d/2) % 8),
+    // which spreads 16 consecutive rows' same chunk over all banks.
+    static constexpr int VT_ROW = BN * 2;  // bytes
+    __device__ static int vtslot(int d, int c) { return c ^ ((d >> 1) & 7); }
 };
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t *p) {
@@ -82,12 +92,62 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t *p) {
 
 // 16 bytes per lane from base + voff + soff straight into LDS (dst + 16*lane).
 // The buffer resource bounds the access to [base, base + nbytes): bytes past
-// the end read as zero.  soff is wave-uniform.
+// the end read as zero.  base, nbytes, dst and soff are wave-uniform.
+//
+// Written as inline assembly so that the compiler does not see an LDS write
+// in flight: it would otherwise wait for every such load to land before the
+// next LDS read of any buffer.  The kernels wait for these loads themselves
+// (s_waitcnt vmcnt) before the barrier that hands the tile to other waves.
+// The instruction has no result register; M0 (the LDS address) is saved and
+// restored around it.
 __device__ __forceinline__ void buffer_load_lds16(const void *base, int nbytes, lds_void *dst, int voff, int soff) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes,
-                                                                         0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 rsrc;
+    rsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+    rsrc[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);               // num_records
+    rsrc[3] = 0x00020000u;                                                    // raw buffer, dword data
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(dst));
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
 }
+
+// Workgroup barrier for LDS traffic only: it waits for this wave's LDS
+// reads and writes but not for its loads still streaming into LDS, which
+// __syncthreads() also drains (its fence counts them as LDS writes).  A
+// wave that filled LDS for others waits for its own loads explicitly before
+// the barrier that publishes them.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Scheduling recipe for a run of NREAD operand reads from LDS, each feeding
+// PER MFMAs: issue PF reads ahead, then alternate PER MFMAs with one read,
+// then drain.  Without it the reads are issued just before their MFMAs and
+// every MFMA waits the full LDS latency.
+template <int NREAD, int PER, int PF>
+__device__ __forceinline__ void sched_read_mfma_pipeline() {
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < NREAD - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF * PER, 0);
+}
+constexpr int PREFETCH = 4;
 
 // {own, partner} values of a lane and lane ^ 32, in either order.
 __device__ __forceinline__ void halves(float x, float &a, float &b) {
@@ -144,11 +204,11 @@ struct Wave {
     using L = Smem<D>;
     bf16x8 qf[RB][D / 16];      // Q^T operand, per row block
     f32x16 oacc[RB][D / 32];    // O^T accumulators
-    float m[RB], l[RB];         // lazy reference max (log2 units) and sum
+    float m[RB], l[RB];         // lazy reference max (log2 units); this lane's half of the sum
     float mtrue[RB];            // exact running max (log2 units)
     int lo_rel[RB], hi_rel[RB]; // visible keys relative to the first tile
     int koff[D / 16];           // K operand read offsets (bytes)
-    int voff[D / 32];           // V^T operand read offsets (bytes)
+    int vko[4];                 // V^T operand read offsets per k-step (bytes)
     int hf;
     float c_log2, scale, softcap;
 
@@ -171,6 +231,7 @@ struct Wave {
                     sacc[r][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                                           qf[r][ds], sacc[r][kb], 0, 0, 0);
             }
+        sched_read_mfma_pipeline<2 * (D / 16), RB, PREFETCH>();
     }
 
     // Online softmax of one tile: masks (if MASK), row max, lazy move of the
@@ -218,17 +279,15 @@ struct Wave {
             const float m_use = m_new == kNegInf ? 0.0f : m_new;
             alpha[r] = fast_exp2(m[r] - m_use);
             m[r] = m_new;
-            float rs = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float pj = EXPLICIT ? fast_exp2(sacc[r][kb][j] - m_use)
+                for (int j = 0; j < 16; ++j)
+                    sacc[r][kb][j] = EXPLICIT ? fast_exp2(sacc[r][kb][j] - m_use)
                                               : fast_exp2(fmaf(sacc[r][kb][j], c_log2, -m_use));
-                    sacc[r][kb][j] = pj;
-                    rs += pj;
-                }
-            l[r] = l[r] * alpha[r] + row_sum(rs);
+            // The row sum of these weights is added in the next matrix phase
+            // (from the bf16 weights P.V uses); here only the rescale.
+            l[r] *= alpha[r];
             // k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16): this lane
             // half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
             // exactly accumulator elements 8*gp .. 8*gp+7.
@@ -255,22 +314,39 @@ struct Wave {
                 for (int j = 0; j < 16; ++j) oacc[r][db][j] *= alpha[r];
     }
 
-    // O^T += V^T P^T.  Two transposing reads give this lane the keys
-    // +4*hf+[0,4) and +8+4*hf+[0,4) of k-step ks at its column db*32 + lane%32.
-    __device__ __forceinline__ void pv(const uint16_t *vbuf, const bf16x8 (&pf)[RB][4]) {
-        const char *Vsb = reinterpret_cast<const char *>(vbuf);
+    // O^T += V^T P^T.  For k-step ks the lane supplies keys ks*16 +
+    // 4*hf + [0,4) and ks*16 + 8 + 4*hf + [0,4) of column db*32 + lane%32:
+    // permuted positions ks*16 + 8*hf + [0,8) of that V^T row, one 16-byte read.
+    __device__ __forceinline__ void pv(const uint16_t *vt, const bf16x8 (&pf)[RB][4]) {
+        const char *Vtb = reinterpret_cast<const char *>(vt);
+        // Row sum of this lane's 32 bf16 weights (dot2 with (1, 1)); the
+        // partner lane's half is added once, in the epilogue.
+        const bf16x2 ones = as_bf16x2(0x3f803f80u);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            float rs = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u32x4 w = __builtin_bit_cast(u32x4, pf[r][k]);
+                const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+                rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w0), ones, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w1), ones, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w2), ones, rs, false);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w3), ones, rs, false);
+            }
+            l[r] += rs;
+        }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const char *base = Vsb + voff[db] + ks * 16 * L::CPR * 16;
-                const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base));
-                const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + 8 * L::CPR * 16));
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(Vtb + db * 32 * L::VT_ROW + vko[ks]);
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
-                    oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r][ks], oacc[r][db], 0, 0, 0);
+                    oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[r][ks],
+                                                                          oacc[r][db], 0, 0, 0);
             }
+        sched_read_mfma_pipeline<4 * (D / 32), RB, PREFETCH>();
     }
 };
 
@@ -281,8 +357,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
     // filled from the buffers being read.
     __shared__ __attribute__((aligned(1024))) uint16_t kbuf0[L::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t kbuf1[L::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t vbuf0[L::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t vbuf1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t vstage[L::TILE];  // V as loaded (row-major)
+    __shared__ __attribute__((aligned(1024))) uint16_t vt0[L::TILE];     // V^T, permuted keys
+    __shared__ __attribute__((aligned(1024))) uint16_t vt1[L::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -349,17 +426,23 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
     // K operand reads: row kb*32 + l32, chunk 2*ds + hf.
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) st.koff[ds] = (l32 * L::CPR + L::kslot(l32, 2 * ds + hf)) * 16;
-    // V^T operand reads: lane in group gq = lane/16 provides row 4*(gq/2) + e
-    // (e = (lane%16)/4; + 16*ks, + 8 for the second read) and column
-    // db*32 + 16*(gq%2) + 4*j (j = lane%4).
-    {
-        const int gq = lane >> 4, e = (lane & 15) >> 2, j = lane & 3;
-        const int row = 4 * (gq >> 1) + e;
+    // V^T operand reads: row d = db*32 + l32, chunk 2*ks + hf.
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int c = db * 4 + 2 * (gq & 1) + (j >> 1);
-            st.voff[db] = (row * L::CPR + L::vslot(row, c)) * 16 + (j & 1) * 8;
-        }
+    for (int ks = 0; ks < 4; ++ks) st.vko[ks] = l32 * L::VT_ROW + L::vtslot(l32, 2 * ks + hf) * 16;
+    // Transposition of the 16 keys 16*lw + [0,16) each loading wave loads:
+    // transposing read t (t < D/16) covers columns 16t + [0,16); lane group
+    // gq = lane/16 provides rows 16*lw + 4*gq + e (e = (lane%16)/4), columns
+    // 16t + 4j (j = lane%4), and receives keys 16*lw + 4*gq + [0,4) of column
+    // 16t + lane%16, written to permuted positions 16*lw + 8*(gq%2) + 4*(gq/2).
+    int tr_src = 0, tr_dst = 0, tr_e = 0, tr_jb = 0;
+    {
+        const int gq = lane >> 4, e = (lane & 15) >> 2, j = lane & 3, i = lane & 15;
+        const int lw0 = wave < LOADERS ? wave : 0;
+        const int rr = 16 * lw0 + 4 * gq + e;
+        tr_src = rr * L::CPR * 16 + (j & 1) * 8;
+        tr_e = rr;
+        tr_jb = j >> 1;
+        tr_dst = i * L::VT_ROW + L::vtslot(i, 2 * lw0 + (gq & 1)) * 16 + 8 * (gq >> 1);
     }
 
     // Direct loads (leader waves only): load u of loader wave lw fills LDS
@@ -385,7 +468,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
         for (int u = 0; u < L::LPW; ++u)
             buffer_load_lds16(K, head_bytes, (lds_void *)(buf + (lw * L::LPW + u) * 64 * 8), k_goff[u], toff);
     };
-    auto load_v = [&](int t, uint16_t *buf) {
+    auto load_v = [&](int t, uint16_t *buf) {  // buf: vstage
         const int toff = (kt0 + t * BN) * D * 2;
 #pragma unroll
         for (int u = 0; u < L::LPW; ++u)
@@ -395,48 +478,65 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
         const int64_t kt = kbeg + (int64_t)t * BN;
         return kt >= full_lo && kt + BN <= full_hi;
     };
+    // This loading wave's 16 keys of the staged V tile -> V^T tile vt.  Only
+    // this wave's own loads are read, so its own wait suffices.
+    auto transpose_v = [&](uint16_t *vt) {
+        const char *src = reinterpret_cast<const char *>(vstage);
+        char *dst = reinterpret_cast<char *>(vt);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            const int c = L::vslot(tr_e, 2 * t + tr_jb);
+            const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(src + tr_src - (tr_src % (L::CPR * 16)) + c * 16 + (tr_src % 16)));
+            *reinterpret_cast<i16x4 *>(dst + tr_dst + 16 * t * L::VT_ROW) = x;
+        }
+    };
 
     f32x16 sacc[RB][2];
     bf16x8 pf[RB][4];
-    // Step j: matrix phase (loads for tiles j+1 / j by the leaders, scores of
-    // tile j from kcur, P.V of tile j-1 from vprev), barrier, vector phase
-    // (softmax of tile j), barrier.  kload/vload receive K of tile j+1 and V
-    // of tile j.
-    auto step = [&](int j, const uint16_t *kcur, const uint16_t *vprev, uint16_t *kload, uint16_t *vload) {
+    // Step j: matrix phase (loads of K for tile j+1 and V for tile j by the
+    // leaders, scores of tile j from kcur, P.V of tile j-1 from vtprev),
+    // barrier, vector phase (softmax of tile j; the leaders then wait for
+    // their loads and transpose their part of V_j into vtcur), barrier.
+    auto step = [&](int j, const uint16_t *kcur, const uint16_t *vtprev, uint16_t *knext, uint16_t *vtcur) {
         if (leader) {
-            if (j + 1 < ntiles) load_k(j + 1, kload);
-            if (j < ntiles) load_v(j, vload);
+            if (j + 1 < ntiles) load_k(j + 1, knext);
+            if (j < ntiles) load_v(j, vstage);
         }
         if (j < ntiles) st.scores(kcur, sacc);
-        if (j >= 1) st.pv(vprev, pf);
-        __syncthreads();
+        if (j >= 1) st.pv(vtprev, pf);
+        lds_barrier();
         if (j < ntiles) {
             float alpha[RB];
             const bool move = is_full(j) ? st.template softmax<false>(sacc, j, pf, alpha)
                                          : st.template softmax<true>(sacc, j, pf, alpha);
             if (move) st.rescale(alpha);
         }
-        if (leader) __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if (leader) {
+            __builtin_amdgcn_s_waitcnt(0);
+            if (j < ntiles) transpose_v(vtcur);
+        }
+        lds_barrier();
     };
 
-    if (leader && ntiles > 0) {
-        load_k(0, kbuf0);
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();
-    if (!leader) __syncthreads();  // trail the leaders by one phase
-    // Tile j's K sits in kbuf[j % 2], its V in vbuf[j % 2].
+    if (leader && ntiles > 0) load_k(0, kbuf0);
+    // Every wave: the Q fragments (so that no wait for them is left inside
+    // the loop, where it would also wait for the tile loads) and the first K
+    // tile.
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    if (!leader) lds_barrier();  // trail the leaders by one phase
+    // Tile j's K sits in kbuf[j % 2], its V^T in vt[j % 2].
     for (int j = 0; j <= ntiles; j += 2) {
-        step(j, kbuf0, vbuf1, kbuf1, vbuf0);
+        step(j, kbuf0, vt1, kbuf1, vt0);
         if (j + 1 > ntiles) break;
-        step(j + 1, kbuf1, vbuf0, kbuf0, vbuf1);
+        step(j + 1, kbuf1, vt0, kbuf0, vt1);
     }
-    if (leader) __syncthreads();  // same barrier count for both groups
+    if (leader) lds_barrier();  // same barrier count for both groups
 
     // ---- epilogue: O = acc / l.  Lane holds dims db*32 + 8*(j/4) + 4*hf + (j%4).
+    const float lr = row_sum(st.l[0]);  // both halves of the row
     if (qrow >= Nq) return;
-    const float lr = st.l[0];
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     const int64_t row = ((int64_t)b * p.H + h) * Nq + qrow;
     if (!SPLIT) {
