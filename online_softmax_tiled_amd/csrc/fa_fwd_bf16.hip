@@ -73,12 +73,19 @@ struct Smem {
     static constexpr int CPR = D / 8;              // 16-byte chunks per row
     static constexpr int TILE = BN * D;            // bf16 elements of one K or V tile
     static constexpr int LPW = BN * CPR / 64 / LOADERS;  // loads per loader wave per tile
-    // Swizzled chunk slot of chunk c in row r.  K: c ^ (r % CPR) puts the
-    // same chunk of 16 consecutive rows in distinct banks.  V: c ^ (4r % CPR)
-    // moves each of the 4 rows a transposing read touches (4 consecutive
-    // rows, 64 bytes each for 32 lanes) to its own 64-byte bank block.
+    // Swizzled chunk slot of chunk c in row r; LDS has 64 banks of 4 bytes
+    // (256 bytes per bank line, RPB = 16 / CPR rows per line).  K: c ^ (r %
+    // CPR) puts the same chunk of 16 consecutive rows in distinct banks.  V
+    // (as loaded): the 32 lanes of one transposing-read pass address rows
+    // {0..3, 8..11} or {4..7, 12..15} of a 16-row group (see the row order of
+    // the transposition below), two chunk halves each; xor-ing the chunk
+    // index with twice (row bits below 2 that select no bank line part, then
+    // row bit 3) gives those 8 rows distinct bank positions.
+    static constexpr int RPB_LOG2 = CPR == 16 ? 0 : (CPR == 8 ? 1 : 2);
     __device__ static int kslot(int r, int c) { return c ^ (r % CPR); }
-    __device__ static int vslot(int r, int c) { return c ^ ((4 * r) % CPR); }
+    __device__ static int vslot(int r, int c) {
+        return c ^ (2 * (((r & 3) >> RPB_LOG2) | (((r >> 3) & 1) << (2 - RPB_LOG2))));
+    }
     // V^T tile: D rows (one per column of V) of BN = 64 permuted keys, 128
     // bytes per row; 16-byte chunk c of row d sits in slot c ^ ((d/2) % 8),
     // which spreads 16 consecutive rows' same chunk over all banks.
@@ -431,18 +438,22 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
     for (int ks = 0; ks < 4; ++ks) st.vko[ks] = l32 * L::VT_ROW + L::vtslot(l32, 2 * ks + hf) * 16;
     // Transposition of the 16 keys 16*lw + [0,16) each loading wave loads:
     // transposing read t (t < D/16) covers columns 16t + [0,16); lane group
-    // gq = lane/16 provides rows 16*lw + 4*gq + e (e = (lane%16)/4), columns
-    // 16t + 4j (j = lane%4), and receives keys 16*lw + 4*gq + [0,4) of column
-    // 16t + lane%16, written to permuted positions 16*lw + 8*(gq%2) + 4*(gq/2).
+    // gq = lane/16 provides rows 16*lw + 4*a + e with a = swap2(gq) (the two
+    // bits of gq exchanged; e = (lane%16)/4), columns 16t + 4j (j = lane%4),
+    // and receives keys 16*lw + 4*a + [0,4) of column 16t + lane%16.  Their
+    // permuted positions are 16*lw + 4*swap2(a) + [0,4) = 16*lw + 4*gq +
+    // [0,4): chunk 2*lw + gq/2, half gq%2, so each 32-lane pass of the
+    // 8-byte writes fills whole chunks.
     int tr_src = 0, tr_dst = 0, tr_e = 0, tr_jb = 0;
     {
         const int gq = lane >> 4, e = (lane & 15) >> 2, j = lane & 3, i = lane & 15;
         const int lw0 = wave < LOADERS ? wave : 0;
-        const int rr = 16 * lw0 + 4 * gq + e;
+        const int a = ((gq & 1) << 1) | (gq >> 1);
+        const int rr = 16 * lw0 + 4 * a + e;
         tr_src = rr * L::CPR * 16 + (j & 1) * 8;
         tr_e = rr;
         tr_jb = j >> 1;
-        tr_dst = i * L::VT_ROW + L::vtslot(i, 2 * lw0 + (gq & 1)) * 16 + 8 * (gq >> 1);
+        tr_dst = i * L::VT_ROW + L::vtslot(i, 2 * lw0 + (gq >> 1)) * 16 + 8 * (gq & 1);
     }
 
     // Direct loads (leader waves only): load u of loader wave lw fills LDS
