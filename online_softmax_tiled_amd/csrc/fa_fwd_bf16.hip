@@ -220,6 +220,7 @@ struct Wave {
     float c_log2, scale, softcap;
 
     // S^T = K Q^T for the 64 keys of a tile, both row blocks.
+    template <bool SCHED = true>
     __device__ __forceinline__ void scores(const uint16_t *kbuf, f32x16 (&sacc)[RB][2]) const {
         const char *Ksb = reinterpret_cast<const char *>(kbuf);
 #pragma unroll
@@ -238,7 +239,7 @@ struct Wave {
                     sacc[r][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                                           qf[r][ds], sacc[r][kb], 0, 0, 0);
             }
-        sched_read_mfma_pipeline<2 * (D / 16), RB, PREFETCH>();
+        if (SCHED) sched_read_mfma_pipeline<2 * (D / 16), RB, PREFETCH>();
     }
 
     // Online softmax of one tile: masks (if MASK), row max, lazy move of the
@@ -258,13 +259,17 @@ struct Wave {
                         sacc[r][kb][j] = CAP ? softcap_log2(sacc[r][kb][j] * scale, softcap) : sacc[r][kb][j] * c_log2;
             }
             if (MASK) {
+                // Key ko = c + 4*hf of the tile is visible iff lo <= ko < hi,
+                // i.e. (unsigned)(c - base) < span: one compare per element.
                 const int lo = lo_rel[r] - it * BN, hi = hi_rel[r] - it * BN;
+                const int base = lo - 4 * hf;
+                const uint32_t span = (uint32_t)(hi - lo);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const int ko = kb * 32 + 8 * (j / 4) + 4 * hf + (j % 4);
-                        if (ko < lo || ko >= hi) sacc[r][kb][j] = kNegInf;
+                        const int c = kb * 32 + 8 * (j / 4) + (j % 4);
+                        if (!((uint32_t)(c - base) < span)) sacc[r][kb][j] = kNegInf;
                     }
             }
             float x = sacc[r][0][0];
@@ -324,6 +329,7 @@ struct Wave {
     // O^T += V^T P^T.  For k-step ks the lane supplies keys ks*16 +
     // 4*hf + [0,4) and ks*16 + 8 + 4*hf + [0,4) of column db*32 + lane%32:
     // permuted positions ks*16 + 8*hf + [0,8) of that V^T row, one 16-byte read.
+    template <bool SCHED = true>
     __device__ __forceinline__ void pv(const uint16_t *vt, const bf16x8 (&pf)[RB][4]) {
         const char *Vtb = reinterpret_cast<const char *>(vt);
         // Row sum of this lane's 32 bf16 weights (dot2 with (1, 1)); the
@@ -353,7 +359,16 @@ struct Wave {
                     oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[r][ks],
                                                                           oacc[r][db], 0, 0, 0);
             }
-        sched_read_mfma_pipeline<4 * (D / 32), RB, PREFETCH>();
+        if (SCHED) sched_read_mfma_pipeline<4 * (D / 32), RB, PREFETCH>();
+    }
+
+    // Scores of one tile and P.V of the previous one as a single operand
+    // pipeline, so the P.V reads start while the last score MFMAs run.
+    __device__ __forceinline__ void matrix(const uint16_t *kbuf, f32x16 (&sacc)[RB][2], const uint16_t *vt,
+                                           const bf16x8 (&pf)[RB][4]) {
+        scores<false>(kbuf, sacc);
+        pv<false>(vt, pf);
+        sched_read_mfma_pipeline<2 * (D / 16) + 4 * (D / 32), RB, PREFETCH>();
     }
 };
 
