@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode]
                     [--no-cpu-baseline] [--no-decode]
+    python bench.py --summarize-profiles DIR   (host only: rocprofv3 CSVs -> profiles/)
 
 A step is one forward pass over one batch of synthetic input:
 
@@ -182,6 +183,153 @@ def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
                       f"{flops / 1e9:.1f} GFLOP fp64 in {secs:.1f} s)"}
 
 
+# rocprofv3 runs whose output --summarize-profiles reads (DIR = their -d root).
+PROFILE_RUNS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
+             "python bench.py --no-cpu-baseline",
+    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE -o run -- "
+                  "python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE -o run -- "
+                  "python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_FETCH_SIZE -o run -- "
+                       "python bench.py --copy-calibration",
+    "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
+                       "python bench.py --copy-calibration",
+}
+KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
+           "combine": "combine_kernel<128>", "copy": "__amd_rocclr_copyBuffer"}
+
+
+def _csv(path):
+    import csv
+    import glob
+    files = glob.glob(path)
+    if not files:
+        raise SystemExit(f"no file matches {path}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_kib(d, run, kernel):
+    """Mean over dispatches of one counter (KiB per dispatch) for `kernel`."""
+    per = {}
+    for r in _csv(os.path.join(d, run, "*counter_collection.csv")):
+        if kernel in r["Kernel_Name"]:
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{run}: no dispatch of {kernel}")
+    return sum(per.values()) / len(per)
+
+
+def summarize_profiles(d):
+    """Write profiles/hbm_traffic.json and the two kernel-trace summaries
+    from the rocprofv3 output under d (the runs in PROFILE_RUNS)."""
+    cmds = {k: v.format(d=d) for k, v in PROFILE_RUNS.items()}
+    stats = {r["Name"]: r for r in _csv(os.path.join(d, "trace", "*kernel_stats.csv"))}
+
+    def stat(kernel):
+        for name, r in stats.items():
+            if kernel in name:
+                return name.replace("void fa::(anonymous namespace)::", ""), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, \
+                    float(r["MaxNs"]) / 1e3
+        raise SystemExit(f"trace: no kernel {kernel}")
+
+    copy_bytes = 1 << 30
+    cf = _counter_kib(d, "copy_FETCH_SIZE", KERNELS["copy"])
+    cw = _counter_kib(d, "copy_WRITE_SIZE", KERNELS["copy"])
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    traffic = {
+        "note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, "
+                "mean over dispatches), each scaled by what the same counter reads for a 1 GiB device copy "
+                "(__amd_rocclr_copyBuffer).  bench.py reports these only while source_hash matches the "
+                "kernel sources.  Written by: python bench.py --summarize-profiles DIR.",
+        "commands": [cmds[k] for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1)},
+    }
+    hbm = {}
+    for kind in ("prefill", "decode", "combine"):
+        f = _counter_kib(d, "FETCH_SIZE", KERNELS[kind])
+        w_ = _counter_kib(d, "WRITE_SIZE", KERNELS[kind])
+        rb, wb = f * 1024 * fs, w_ * 1024 * ws
+        hbm[kind] = (rb, wb)
+        rec = {"kernel": KERNELS[kind], "fetch_kib_per_dispatch": round(f, 1),
+               "write_kib_per_dispatch": round(w_, 1), "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+               "bytes_per_launch": int(round(rb + wb))}
+        if kind in KERNEL_SOURCES:
+            rec["source_hash"] = source_hash(kind)
+        traffic[kind] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+
+    wp, wd = wl.WORKLOADS[PREFILL], wl.WORKLOADS[DECODE]
+    name, calls, avg, mn, mx = stat(KERNELS["prefill"])
+    flops = wl.algorithmic_flops(wp)
+    rb, wb = hbm["prefill"]
+    md = f"""# fwd_bf16_kernel on the causal prefill workload (B=4, H=32, Nq=Nk=4096, d=128, bf16)
+
+Command (run from the repository root on one MI355X):
+
+    {cmds["trace"]}
+
+Kernel trace statistics (`run_kernel_stats.csv`; every dispatch of the run,
+the bench's warm-up launches included):
+
+| kernel | calls | average (us) | min (us) | max (us) |
+|---|---|---|---|---|
+| {name[:90]} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |
+
+Algorithmic work per launch: {flops:,} FLOP (4*d per visible query-key pair,
+N(N+1)/2 pairs per head).  At the trace's average duration this is
+{flops / (avg * 1e-6) / 1e12:.0f} TFLOP/s ({flops / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS * 100:.1f}% of the 2.5 PFLOP/s dense bf16 peak);
+at the minimum, {flops / (mn * 1e-6) / 1e12:.0f} TFLOP/s.
+
+HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
+scaled by a 1 GiB copy; see hbm_traffic.json for the commands): read {rb / 1e6:.1f} MB,
+written {wb / 1e6:.1f} MB, total {(rb + wb) / 1e6:.1f} MB, against {wl.algorithmic_bytes(wp) / 1e6:.1f} MB of
+algorithmic bytes (Q, K, V read once, O and lse written once): the re-reads
+of K and V by the 16 query tiles of each head are served from L2 / MALL.
+"""
+    with open(os.path.join(ROOT, "profiles", f"fwd_bf16_causal_b4_h32_n4096_d128.md"), "w") as f:
+        f.write(md)
+
+    name, calls, avg, mn, mx = stat(KERNELS["decode"])
+    cname, ccalls, cavg, cmn, cmx = stat(KERNELS["combine"])
+    S = wd.num_splits
+    part_bytes = wd.B * wd.H * wd.Nq * S * (wd.d + 2) * 4
+    split_bytes = wl.algorithmic_bytes(wd) - part_bytes - (wd.B * wd.H * wd.Nq * (wd.d * 2 + 4))
+    rb, wb = hbm["decode"]
+    crb, cwb = hbm["combine"]
+    md = f"""# splitkv_decode_kernel + combine_kernel on the split-KV decode workload (B=16, H=32, Hkv=8, Nq=1, Nk=32768, d=128, 16 splits, bf16)
+
+Command (run from the repository root on one MI355X):
+
+    {cmds["trace"]}
+
+Kernel trace statistics (`run_kernel_stats.csv`; the bench runs the split
+kernel both inside split+combine steps and alone, warm-up included):
+
+| kernel | calls | average (us) | min (us) | max (us) |
+|---|---|---|---|---|
+| {name[:90]} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |
+| {cname[:90]} | {ccalls} | {cavg:.1f} | {cmn:.1f} | {cmx:.1f} |
+
+Algorithmic bytes of the split kernel per launch: {split_bytes:,} (K and V
+read once per K/V head, Q read, fp32 partials written).  At the trace's
+average duration: {split_bytes / (avg * 1e-6) / 1e9:.0f} GB/s ({split_bytes / (avg * 1e-6) / 1e9 / PEAK_HBM_GBS * 100:.1f}% of the 8 TB/s HBM3E peak).
+Split + combine: {avg + cavg:.1f} us for {wl.algorithmic_bytes(wd):,} algorithmic bytes,
+{wl.algorithmic_bytes(wd) / ((avg + cavg) * 1e-6) / 1e9:.0f} GB/s ({wl.algorithmic_bytes(wd) / ((avg + cavg) * 1e-6) / 1e9 / PEAK_HBM_GBS * 100:.1f}%).
+
+HBM traffic per launch (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy; see
+hbm_traffic.json): split kernel read {rb / 1e9:.3f} GB, written {wb / 1e6:.2f} MB
+(algorithmic {split_bytes / 1e9:.3f} GB); combine {(crb + cwb) / 1e6:.2f} MB
+(algorithmic {part_bytes / 1e6:.2f} MB of partials read + {wd.B * wd.H * wd.Nq * (wd.d * 2 + 4) / 1e6:.2f} MB of O and lse written).
+"""
+    with open(os.path.join(ROOT, "profiles", f"splitkv_decode_b16_h32kv8_nk32768_d128.md"), "w") as f:
+        f.write(md)
+    print(json.dumps({k: traffic[k]["bytes_per_launch"] for k in ("prefill", "decode", "combine")}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,7 +340,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="host only: write profiles/ from the rocprofv3 output under DIR")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
