@@ -361,15 +361,6 @@ struct Wave {
             }
         if (SCHED) sched_read_mfma_pipeline<4 * (D / 32), RB, PREFETCH>();
     }
-
-    // Scores of one tile and P.V of the previous one as a single operand
-    // pipeline, so the P.V reads start while the last score MFMAs run.
-    __device__ __forceinline__ void matrix(const uint16_t *kbuf, f32x16 (&sacc)[RB][2], const uint16_t *vt,
-                                           const bf16x8 (&pf)[RB][4]) {
-        scores<false>(kbuf, sacc);
-        pv<false>(vt, pf);
-        sched_read_mfma_pipeline<2 * (D / 16) + 4 * (D / 32), RB, PREFETCH>();
-    }
 };
 
 template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
