@@ -53,7 +53,7 @@ def _bind(lib):
         dp, dp, dp, dp, dp, dp, dp,
         i64, i64, i64, i64, i64, i64,
         ctypes.c_double, ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_double,
-        i64, i64, ctypes.POINTER(i64), i64, i64, ctypes.c_int]
+        i64, i64, i64, ctypes.POINTER(i64), i64, i64, ctypes.c_int]
     lib.oracle_combine.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64]
     return lib
@@ -81,14 +81,15 @@ def default_threads() -> int:
 def attention(q, k, v, scale: float, causal: bool = False, window: int = 0,
               head_window=None, softcap: float = 0.0, rows=None,
               key_range=None, tile: int = 0, nthreads: int | None = None,
-              lib=None):
+              lib=None, sinks: int = 0):
     """Exact attention of every row (or of the listed ``rows``).
 
     ``head_window`` (int sequence of length H) overrides ``window`` per query
     head.  ``rows`` are flat indices r = (b*H + h)*Nq + i.  ``key_range``
     (lo, hi) restricts the keys, as one split of the key axis does.
     ``tile`` > 0 runs the streaming recurrence with that many keys per tile
-    instead of the direct definition.
+    instead of the direct definition.  ``sinks`` > 0 keeps keys j < sinks
+    visible to windowed rows (attention sinks, Transformers & Math 16.6).
 
     Returns dict(o, lse, m, l): o is [B,H,Nq,d] (or [len(rows), d]); lse, m
     and l are [B,H,Nq] (or [len(rows)]); m and l are the row maximum and the
@@ -119,7 +120,7 @@ def attention(q, k, v, scale: float, causal: bool = False, window: int = 0,
     rc = lib.oracle_attention(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(m), _ptr(ell),
         B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _ptr(hw, ctypes.c_int32),
-        float(softcap), int(lo), int(hi),
+        float(softcap), int(sinks), int(lo), int(hi),
         _ptr(rows_arr, ctypes.c_int64), n, int(tile),
         int(nthreads if nthreads is not None else default_threads()))
     if rc != 0:

@@ -32,6 +32,10 @@
  *     query aligned with the last key); causal keeps j <= p;
  *   - a window W > 0 keeps p - W < j, i.e. exactly W keys including the
  *     query's own position; it is defined only together with causal;
+ *   - attention sinks (section 16.6, streaming: the first 4 tokens are
+ *     always kept alongside the sliding window): with sinks = S > 0 the
+ *     keys j < S stay visible to a windowed row whatever its window (still
+ *     subject to the causal rule j <= p);
  *   - query head h reads key/value head g = h / (H / Hkv);
  *   - a row with no visible key gets O = 0, lse = -inf, m = -inf, l = 0;
  *   - the mask is applied after the cap (masked keys never contribute).
@@ -53,6 +57,7 @@ typedef struct {
     int causal;
     const int32_t *head_window; /* [H]; <= 0 means no window for that head */
     double softcap;             /* <= 0 disables the cap */
+    int64_t sinks;              /* keys j < sinks ignore the window */
     int64_t key_lo, key_hi;     /* keys outside [key_lo, key_hi) are excluded */
     const int64_t *rows;        /* NULL: all rows; else nrows row indices    */
     int64_t nrows;
@@ -67,7 +72,7 @@ static int visible(const job_t *J, int64_t h, int64_t i, int64_t j)
     int32_t W = J->head_window ? J->head_window[h] : 0;
     if (j < J->key_lo || j >= J->key_hi) return 0;
     if (J->causal && j > p) return 0;
-    if (W > 0 && j <= p - W) return 0;
+    if (W > 0 && j <= p - W && j >= J->sinks) return 0;
     return 1;
 }
 
@@ -189,6 +194,7 @@ static void *worker(void *arg)
  *       outputs [B*H*Nq]; otherwise nrows row indices, writing o [nrows, d].
  * o, lse, m_out, l_out: any may be NULL.  m_out/l_out receive the row max
  *       and sum exp(s - m) (the (m, l) of the merge equations).
+ * sinks: keys j < sinks are exempt from the window (attention sinks).
  * key_lo, key_hi: restrict the keys to [key_lo, key_hi) (one split's chunk).
  * nthreads: worker threads over rows (<= 0: one).
  * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure.
@@ -197,11 +203,11 @@ int oracle_attention(const double *q, const double *k, const double *v,
                      double *o, double *lse, double *m_out, double *l_out,
                      int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                      double scale, int causal, const int32_t *head_window, double softcap,
-                     int64_t key_lo, int64_t key_hi,
+                     int64_t sinks, int64_t key_lo, int64_t key_hi,
                      const int64_t *rows, int64_t nrows, int64_t tile, int nthreads)
 {
     if (B < 0 || H < 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d < 0) return -1;
-    if (H % Hkv != 0 || tile < 0) return -1;
+    if (H % Hkv != 0 || tile < 0 || sinks < 0) return -1;
     if (head_window) {
         for (int64_t h = 0; h < H; ++h)
             if (head_window[h] > 0 && !causal) return -1;
@@ -221,6 +227,7 @@ int oracle_attention(const double *q, const double *k, const double *v,
     base.B = B; base.H = H; base.Hkv = Hkv; base.Nq = Nq; base.Nk = Nk; base.d = d;
     base.scale = scale; base.causal = causal; base.head_window = head_window;
     base.softcap = softcap;
+    base.sinks = sinks;
     base.key_lo = key_lo < 0 ? 0 : key_lo;
     base.key_hi = key_hi > Nk ? Nk : key_hi;
     base.rows = rows; base.nrows = nrows; base.tile = tile;

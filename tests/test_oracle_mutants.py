@@ -24,7 +24,11 @@ MUTANTS = {
     "wrong_group_index": ("int64_t g = h / (J->H / J->Hkv);\n    const double *qr",
                           "int64_t g = h % J->Hkv;\n    const double *qr"),
     "causal_off_by_one": ("if (J->causal && j > p) return 0;", "if (J->causal && j >= p) return 0;"),
-    "window_off_by_one": ("if (W > 0 && j <= p - W) return 0;", "if (W > 0 && j < p - W) return 0;"),
+    "window_off_by_one": ("if (W > 0 && j <= p - W && j >= J->sinks) return 0;",
+                          "if (W > 0 && j < p - W && j >= J->sinks) return 0;"),
+    "sinks_ignored": ("if (W > 0 && j <= p - W && j >= J->sinks) return 0;", "if (W > 0 && j <= p - W) return 0;"),
+    "sinks_off_by_one": ("if (W > 0 && j <= p - W && j >= J->sinks) return 0;",
+                         "if (W > 0 && j <= p - W && j > J->sinks) return 0;"),
     "top_left_alignment": ("int64_t p = i + (J->Nk - J->Nq);", "int64_t p = i;"),
     "cap_not_rescaled": ("s = J->softcap * tanh(s / J->softcap);", "s = tanh(s / J->softcap);"),
     "keys_read_from_values": ("const double *kr = J->k +", "const double *kr = J->v +"),
@@ -117,6 +121,13 @@ def _battery(lib):
         o, lse = oracle.combine(op, mp, lp, lib=lib)
         return np.allclose(o, full["o"], atol=1e-13) and np.allclose(lse, full["lse"], atol=1e-13)
 
+    def sinks():
+        qs, ks, vs = rng.standard_normal((1, 1, 3, 2)), rng.standard_normal((1, 1, 9, 2)), \
+            rng.standard_normal((1, 1, 9, 2))
+        o_ref, lse_ref = brute_force(qs, ks, vs, 0.9, True, [2], 0.0, sinks=3)
+        r = A(qs, ks, vs, 0.9, causal=True, head_window=[2], sinks=3)
+        return np.allclose(r["o"], o_ref, atol=1e-12) and np.allclose(r["lse"], lse_ref, atol=1e-12)
+
     def tiling():
         d = A(q, k, v, 0.8, causal=True)
         return all(np.allclose(A(q, k, v, 0.8, causal=True, tile=t)["o"], d["o"], atol=1e-13)
@@ -126,7 +137,7 @@ def _battery(lib):
                      ("brute_force", brute), ("uniform_counts", uniform_counts),
                      ("softcap_values", softcap_values), ("gqa", gqa),
                      ("merge_exercise", merge_exercise), ("split_invariance", split_invariance),
-                     ("tiling", tiling)]:
+                     ("tiling", tiling), ("sinks", sinks)]:
         check(name, fn)
     return failed
 

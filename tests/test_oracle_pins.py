@@ -33,20 +33,21 @@ def _dtanh(x: Decimal) -> Decimal:
     return (e - 1) / (e + 1)
 
 
-def _visible_keys(i, Nq, Nk, causal, W):
+def _visible_keys(i, Nq, Nk, causal, W, sinks=0):
     """The keys a query sees, built as explicit position sets: every key, or
     the keys at or before the query's absolute position i + Nk - Nq, and of
-    those only the W most recent when a window is set."""
+    those only the W most recent when a window is set, together with the
+    first ``sinks`` positions (attention sinks, Transformers & Math 16.6)."""
     p = i + Nk - Nq
     keys = set(range(Nk))
     if causal:
         keys &= set(range(0, p + 1))
     if W > 0:
-        keys &= set(range(p - W + 1, p + 1))
+        keys &= set(range(p - W + 1, p + 1)) | set(range(0, sinks))
     return sorted(keys)
 
 
-def brute_force(q, k, v, scale, causal=False, head_window=None, softcap=0.0):
+def brute_force(q, k, v, scale, causal=False, head_window=None, softcap=0.0, sinks=0):
     """O and lse by the probability form p_j = 1 / sum_k exp(s_k - s_j),
     in 50-digit decimal arithmetic; no running or global maximum."""
     B, H, Nq, d = q.shape
@@ -59,7 +60,7 @@ def brute_force(q, k, v, scale, causal=False, head_window=None, softcap=0.0):
         for h in range(H):
             g = h // (H // Hkv)
             for i in range(Nq):
-                keys = _visible_keys(i, Nq, Nk, causal, hw[h])
+                keys = _visible_keys(i, Nq, Nk, causal, hw[h], sinks)
                 if not keys:
                     continue
                 s = {}
@@ -392,3 +393,82 @@ def test_merge_with_empty_partial_is_identity():
     assert np.allclose(lse, m_part[:, 0] + np.log(l_part[:, 0]), rtol=1e-15, atol=0)
     o, lse = oracle.combine(np.zeros((2, 3, 4)), np.full((2, 3), -np.inf), np.zeros((2, 3)))
     assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# Attention sinks with a sliding window (Transformers & Math 16.3 and 16.6):
+# the first tokens stay visible to every windowed query.
+SINK_CASES = [
+    # B, H, Hkv, Nq, Nk, d, scale, head_window, softcap, sinks
+    (1, 2, 1, 6, 9, 2, 1.0, [3, 2], 0.0, 2),
+    (1, 1, 1, 5, 12, 3, 1.2, [2], 0.0, 4),
+    (1, 2, 2, 4, 7, 2, 0.9, [1, 0], 2.0, 3),
+    (1, 1, 1, 3, 3, 2, 1.0, [1], 0.0, 1),
+]
+
+
+@pytest.mark.parametrize("n", range(len(SINK_CASES)))
+def test_sinks_match_decimal_brute_force(n):
+    B, H, Hkv, Nq, Nk, d, scale, hw, cap, S = SINK_CASES[n]
+    rng = np.random.default_rng(300 + n)
+    q, k, v = _rand((B, H, Nq, d), rng), _rand((B, Hkv, Nk, d), rng), _rand((B, Hkv, Nk, d), rng)
+    o_ref, lse_ref = brute_force(q, k, v, scale, True, hw, cap, sinks=S)
+    r = oracle.attention(q, k, v, scale, causal=True, head_window=hw, softcap=cap, sinks=S)
+    assert np.allclose(r["o"], o_ref, rtol=0, atol=1e-13)
+    assert np.allclose(r["lse"], lse_ref, rtol=1e-14, atol=1e-13)
+
+
+def test_sinks_covering_every_position_is_plain_causal():
+    rng = np.random.default_rng(5)
+    q, k, v = _rand((1, 2, 5, 3), rng), _rand((1, 2, 8, 3), rng), _rand((1, 2, 8, 3), rng)
+    a = oracle.attention(q, k, v, 0.7, causal=True, window=2, sinks=8)
+    b = oracle.attention(q, k, v, 0.7, causal=True)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
+
+
+def test_sinks_need_no_window_to_matter():
+    # without a window every causal key is visible anyway: sinks change nothing
+    rng = np.random.default_rng(6)
+    q, k, v = _rand((1, 1, 4, 3), rng), _rand((1, 1, 6, 3), rng), _rand((1, 1, 6, 3), rng)
+    a = oracle.attention(q, k, v, 0.7, causal=True, sinks=3)
+    b = oracle.attention(q, k, v, 0.7, causal=True)
+    assert np.array_equal(a["o"], b["o"])
+
+
+def test_uniform_scores_with_sinks_average_sink_and_window_values():
+    # zero queries: every visible key has the same score, so O is the mean of
+    # the visible values and lse the log of their count
+    rng = np.random.default_rng(8)
+    Nk, W, S = 20, 5, 4
+    k, v = _rand((1, 1, Nk, 2), rng), _rand((1, 1, Nk, 2), rng)
+    r = oracle.attention(np.zeros((1, 1, 1, 2)), k, v, 1.0, causal=True, window=W, sinks=S)
+    keys = list(range(S)) + list(range(Nk - W, Nk))
+    assert abs(r["lse"][0, 0, 0] - np.log(len(keys))) < 1e-14
+    assert np.allclose(r["o"][0, 0, 0], v[0, 0, keys].mean(0), atol=1e-15)
+
+
+def _ring_rows(pos, window, sinks):
+    """Rows of a rolling cache (sinks rows first, then a ring of window slots)
+    and the absolute position each holds after tokens 0..pos were written:
+    token t < sinks goes to row t, token t >= sinks to row sinks + (t -
+    sinks) % window, a later token replacing an earlier one."""
+    rows = {}
+    for t in range(pos + 1):
+        rows[t if t < sinks else sinks + (t - sinks) % window] = t
+    return rows
+
+
+@pytest.mark.parametrize("pos,W,S", [(2, 4, 4), (6, 4, 4), (7, 4, 4), (30, 4, 4), (31, 5, 0), (9, 3, 2)])
+def test_rolling_cache_equals_sink_window_attention(pos, W, S):
+    # the decode query at position pos attending to every filled row of the
+    # rolling cache sees exactly the sink + window keys of the full sequence
+    rng = np.random.default_rng(pos * 10 + W)
+    N, d = pos + 1, 3
+    q, k, v = _rand((1, 2, 1, d), rng), _rand((1, 1, N, d), rng), _rand((1, 1, N, d), rng)
+    rows = _ring_rows(pos, W, S)
+    n = len(rows)
+    assert sorted(rows) == list(range(n))  # filled rows form a prefix of the cache
+    idx = [rows[r] for r in range(n)]
+    ref = oracle.attention(q, k, v, 0.6, causal=True, window=W, sinks=S)
+    got = oracle.attention(q, k[:, :, idx], v[:, :, idx], 0.6)
+    assert np.allclose(got["o"], ref["o"], rtol=0, atol=1e-14)
+    assert np.allclose(got["lse"], ref["lse"], rtol=0, atol=1e-14)
