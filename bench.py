@@ -11,7 +11,11 @@ A step is one forward pass over one batch of synthetic input:
   (B=4, H=32, 4096 x 4096, d=128) -- the headline TFLOP/s figure;
 * decode (also measured in the same run unless ``--no-decode``):
   ``fa_fwd_splitkv`` + ``fa_combine`` on the split-KV decode workload
-  (B=16, H=32, Hkv=8, Nk=32768, d=128, 16 splits), in GB/s.
+  (B=16, H=32, Hkv=8, Nk=32768, d=128, 16 splits), in GB/s;
+* rolling (same condition): streaming decode over a rolling KV cache with
+  attention sinks -- ``fa_kv_append`` of one token + ``fa_decode_rolling``
+  + ``fa_combine`` (B=16, H=32, Hkv=8, d=128, window 4096, 4 sinks, 4
+  splits, position 65535), in GB/s.
 
 Inputs are seeded synthetic tensors (online_softmax_tiled_amd.workloads),
 resident in HBM before timing starts.  Kernel durations are taken with HIP
@@ -148,6 +152,54 @@ def bench_decode(torch, fa, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
                      "kernel": "splitkv_decode_kernel", "avg_ms": round(avg_split, 4)},
+    }
+
+
+def bench_rolling(torch, fa, steps, warmup):
+    """Streaming decode over a rolling KV cache with attention sinks: a step
+    appends one token's K/V (fa_kv_append) and runs fa_decode_rolling +
+    fa_combine for its query, at a fixed position far into the stream."""
+    w = wl.ROLLING
+    rng = np.random.default_rng(w.seed)
+
+    def rand(*shape):
+        return torch.from_numpy(wl.round_bf16(rng.standard_normal(shape).astype(np.float32))) \
+            .to(torch.bfloat16).cuda()
+
+    rows = w.sinks + w.window
+    kc, vc = rand(w.B, w.Hkv, rows, w.d), rand(w.B, w.Hkv, rows, w.d)
+    kn, vn = rand(w.B, w.Hkv, 1, w.d), rand(w.B, w.Hkv, 1, w.d)
+    q = rand(w.B, w.H, 1, w.d)
+    S = w.num_splits
+    o_part = torch.empty((w.B, w.H, 1, S, w.d), dtype=torch.float32, device="cuda")
+    m_part = torch.empty((w.B, w.H, 1, S), dtype=torch.float32, device="cuda")
+    l_part = torch.empty_like(m_part)
+    o = torch.empty((w.B, w.H, 1, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
+
+    def decode():
+        fa.fa_decode_rolling(q, kc, vc, o_part, m_part, l_part, w.B, w.H, w.Hkv, w.d, w.pos, w.window, w.sinks,
+                             w.scale, 0.0, S)
+
+    def launch():
+        fa.fa_kv_append(kn, vn, kc, vc, w.B, w.Hkv, 1, w.d, w.pos, w.window, w.sinks)
+        decode()
+        fa.fa_combine(o_part, m_part, l_part, o, lse, w.B, w.H, 1, w.d, S, 0)
+
+    avg, total, wall = time_launches(launch, steps, warmup, torch)
+    avg_dec, _, _ = time_launches(decode, steps, 2, torch)
+    nbytes = wl.rolling_bytes(w)
+    dec_bytes = 2 * w.rows * w.B * w.Hkv * w.d * 2 + w.B * w.H * w.d * 2 + w.B * w.H * S * (w.d + 2) * 4
+    achieved = dec_bytes / (avg_dec * 1e-3) / 1e9
+    return {
+        "workload": w.name, "value": round(nbytes * steps / (total * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "ms_per_step": round(total / steps, 4), "frac_of_hbm_peak": round(nbytes * steps / (total * 1e-3) / 1e9
+                                                                        / PEAK_HBM_GBS, 4),
+        "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "d": w.d, "window": w.window, "sinks": w.sinks,
+                   "pos": w.pos, "cache_rows_read": w.rows, "num_splits": S},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "splitkv_decode_kernel (rolling cache)", "avg_ms": round(avg_dec, 4)},
     }
 
 
@@ -337,7 +389,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", choices=["prefill", "decode"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="prefill leg only (no decode or rolling legs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -365,13 +417,16 @@ def main():
     torch.cuda.init()
 
     main_w, leg = None, None
-    decode = None
+    decode = rolling = None
     if args.workload == "prefill":
         main_w, leg = bench_prefill(torch, fa, args.steps, args.warmup)
         print(f"[bench] prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
         if not args.no_decode:
             dw, decode = bench_decode(torch, fa, args.steps, args.warmup)
             print(f"[bench] decode done: {decode['avg_ms']:.3f} ms/step", file=sys.stderr, flush=True)
+            rolling = bench_rolling(torch, fa, args.steps, args.warmup)
+            print(f"[bench] rolling decode done: {rolling['ms_per_step']:.4f} ms/step", file=sys.stderr,
+                  flush=True)
         value, unit = leg["value"], "TFLOP/s"
     else:
         main_w, leg = bench_decode(torch, fa, args.steps, args.warmup)
@@ -393,6 +448,8 @@ def main():
                          "ms_per_step": round(decode["total_ms"] / args.steps, 4),
                          "frac_of_hbm_peak": round(decode["value"] / PEAK_HBM_GBS, 4),
                          "roofline": decode["roofline"]}
+    if rolling is not None:
+        out["rolling"] = rolling
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)

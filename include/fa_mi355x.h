@@ -160,6 +160,56 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part,
                void *o, float *lse, int64_t B, int64_t H, int64_t Nq, int64_t d,
                int num_splits, int out_dtype, fa_stream_t stream);
 
+/*
+ * Rolling KV cache with attention sinks, for streaming decode.
+ *
+ * Transformers & Math section 16.3: a local (sliding-window) layer attends
+ * to the W most recent tokens only, so its cache never holds more than W
+ * entries; section 16.6: streaming keeps the first few tokens (attention
+ * sinks, 4 in the setup it describes) alongside the window.  A cache of one
+ * such layer is two bf16 tensors k_cache, v_cache [B, Hkv, sinks + window, d]
+ * (row-major, caller-owned, device memory): rows [0, sinks) hold tokens
+ * 0 .. sinks-1 for good, rows [sinks, sinks + window) are a ring in which
+ * token t >= sinks lives in row sinks + (t - sinks) % window until token
+ * t + window replaces it.  After tokens 0 .. pos were written, the filled
+ * rows are the prefix [0, min(pos + 1, sinks + window)) and hold exactly the
+ * sink tokens and the window of the W most recent tokens.
+ */
+
+/*
+ * fa_kv_append -- write the K and V rows of tokens pos .. pos+T-1 into a
+ * rolling cache.  k_new, v_new: bf16 [B, Hkv, T, d] (device); k_cache,
+ * v_cache as above.  Token t goes to row t if t < sinks, else to row
+ * sinks + (t - sinks) % window; when two of the T tokens map to one row the
+ * later one is written.  Asynchronous on stream.
+ * Errors: FA_ERR_INVALID_ARG for negative sizes, pos < 0, window < 1,
+ * sinks < 0, NULL pointers when B*Hkv*T*d > 0; FA_ERR_UNSUPPORTED for d not
+ * in {32, 64, 128}.
+ */
+int fa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                 int64_t B, int64_t Hkv, int64_t T, int64_t d,
+                 int64_t pos, int64_t window, int64_t sinks, fa_stream_t stream);
+
+/*
+ * fa_decode_rolling -- split-KV first pass for the query of the token at
+ * position pos against a rolling cache that holds tokens 0 .. pos (its own
+ * K/V included: append first).  q: bf16 [B, H, 1, d]; query head h reads
+ * cache head h / (H / Hkv).  The filled rows [0, n) with
+ * n = min(pos + 1, sinks + window) are cut into num_splits chunks of
+ * ceil(n / num_splits) rows, and the partials are written exactly as by
+ * fa_fwd_splitkv with Nq = 1 (o_part [B,H,1,S,d], m_part and l_part
+ * [B,H,1,S], fp32); fa_combine(..., Nq = 1, ...) then gives the output and
+ * lse.  The result is attention of that query over the sink tokens and the
+ * window of the W most recent tokens, each once.  scale and softcap as
+ * fa_fwd.  Errors as fa_kv_append, plus FA_ERR_INVALID_ARG for
+ * num_splits < 1, H % Hkv != 0, non-finite scale or softcap < 0.
+ */
+int fa_decode_rolling(const void *q, const void *k_cache, const void *v_cache,
+                      float *o_part, float *m_part, float *l_part,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t d,
+                      int64_t pos, int64_t window, int64_t sinks,
+                      float scale, float softcap, int num_splits, fa_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *fa_status_string(int status);
 

@@ -6,12 +6,15 @@ is loaded on first use and every entry point raises if it is missing.
 """
 from .fa import (  # noqa: F401
     FaError,
+    RollingKVCache,
     attention,
     fa_combine,
+    fa_decode_rolling,
     fa_fwd,
     fa_fwd_ex,
     fa_fwd_f32,
     fa_fwd_splitkv,
+    fa_kv_append,
     fa_status_string,
     library_path,
     load_library,

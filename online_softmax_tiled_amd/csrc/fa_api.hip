@@ -48,6 +48,7 @@ int validate_fwd(const fa_fwd_args &a, FwdParams &p) {
     p.Hkv = a.Hkv;
     p.Nq = a.Nq;
     p.Nk = a.Nk;
+    p.kv_rows = a.Nk;
     p.group = (int)(a.H / a.Hkv);
     p.num_splits = 1;
     p.split_len = 0;
@@ -70,6 +71,32 @@ int run_fwd(const fa_fwd_args &a) {
     hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
     if (a.dtype == FA_DTYPE_FP32) return fa::launch_fwd_f32(p, (int)a.d, s);
     return fa::launch_fwd_bf16(p, (int)a.d, false, s);
+}
+
+// First pass of split-KV attention for validated parameters p (num_splits
+// >= 1, partial pointers checked): the decode kernel when few query rows
+// share a K/V head, the MFMA kernel in split mode otherwise.
+int run_splitkv(FwdParams &p, float *o_part, float *m_part, float *l_part, int num_splits, int64_t d,
+                fa_stream_t stream) {
+    if (p.B == 0 || p.H == 0 || p.Nq == 0) return FA_OK;
+    const int64_t split_len = (p.Nk + num_splits - 1) / num_splits;
+    if (split_len > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    p.o = nullptr;
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+    p.num_splits = num_splits;
+    p.split_len = (int)split_len;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if ((int64_t)p.group * p.Nq <= fa::splitkv_decode_max_rows()) return fa::launch_splitkv_decode(p, (int)d, s);
+    return fa::launch_fwd_bf16(p, (int)d, true, s);
+}
+
+// Rolling-cache geometry: window >= 1, sinks >= 0, pos >= 0, and sizes that
+// keep row indices in range.
+bool valid_rolling(int64_t pos, int64_t window, int64_t sinks) {
+    const int64_t lim = (int64_t)1 << 40;
+    return pos >= 0 && window >= 1 && sinks >= 0 && window < lim && sinks < lim && pos < ((int64_t)1 << 62);
 }
 
 fa_fwd_args make_args(int dtype, const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
@@ -133,18 +160,36 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o_part, f
     const int rc = validate_fwd(a, p);
     if (rc != FA_OK) return rc;
     if (B * H * Nq > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
-    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
-    const int64_t split_len = (Nk + num_splits - 1) / num_splits;
-    if (split_len > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    p.o = nullptr;
-    p.o_part = o_part;
-    p.m_part = m_part;
-    p.l_part = l_part;
-    p.num_splits = num_splits;
-    p.split_len = (int)split_len;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if ((int64_t)p.group * Nq <= fa::splitkv_decode_max_rows()) return fa::launch_splitkv_decode(p, (int)d, s);
-    return fa::launch_fwd_bf16(p, (int)d, true, s);
+    return run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
+}
+
+int fa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache, int64_t B, int64_t Hkv,
+                 int64_t T, int64_t d, int64_t pos, int64_t window, int64_t sinks, fa_stream_t stream) {
+    if (B < 0 || Hkv < 0 || T < 0 || d < 0 || !valid_rolling(pos, window, sinks)) return FA_ERR_INVALID_ARG;
+    const int64_t n_rows = B * Hkv * T;
+    if (n_rows > 0 && d > 0 && (!k_new || !v_new || !k_cache || !v_cache)) return FA_ERR_INVALID_ARG;
+    if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+    return fa::launch_kv_append(k_new, v_new, k_cache, v_cache, n_rows, T, pos, window, sinks, (int)d,
+                                reinterpret_cast<hipStream_t>(stream));
+}
+
+int fa_decode_rolling(const void *q, const void *k_cache, const void *v_cache, float *o_part, float *m_part,
+                      float *l_part, int64_t B, int64_t H, int64_t Hkv, int64_t d, int64_t pos, int64_t window,
+                      int64_t sinks, float scale, float softcap, int num_splits, fa_stream_t stream) {
+    if (num_splits < 1 || !valid_rolling(pos, window, sinks)) return FA_ERR_INVALID_ARG;
+    const int64_t rows = sinks + window;                  // cache rows per (batch, K/V head)
+    const int64_t n = pos + 1 < rows ? pos + 1 : rows;    // filled rows: sinks and the window
+    // Every filled row is visible to this query: no causal or window mask
+    // over the cache rows.  o is not written by this pass (stand-in).
+    fa_fwd_args a = make_args(FA_DTYPE_BF16, q, k_cache, v_cache, o_part, nullptr, B, H, Hkv, 1, n, d, scale, 0, 0,
+                              softcap, stream);
+    FwdParams p;
+    const int rc = validate_fwd(a, p);
+    if (rc != FA_OK) return rc;
+    if (rows * d > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    if (B * H > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
+    p.kv_rows = rows;
+    return run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
 }
 
 int fa_combine(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse, int64_t B,

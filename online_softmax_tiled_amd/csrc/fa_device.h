@@ -36,6 +36,7 @@ struct FwdParams {
     float *lse;
     float *o_part, *m_part, *l_part;  // split-KV outputs (NULL otherwise)
     int64_t B, H, Hkv, Nq, Nk;
+    int64_t kv_rows;   // rows per (batch, K/V head) in the K and V buffers (>= Nk)
     int group;         // H / Hkv
     int num_splits;    // 1 unless split-KV
     int split_len;     // keys per split (ceil(Nk / num_splits))

@@ -405,8 +405,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
     const int64_t full_hi = hi_first < r_hi ? hi_first : r_hi;
 
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.H + h) * Nq * D;
-    const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * Nk * D;
-    const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * Nk * D;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
 
     Wave<D, EXPLICIT, CAP> st;
     st.hf = hf;

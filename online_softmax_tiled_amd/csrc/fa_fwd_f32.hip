@@ -44,8 +44,8 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(const FwdParams p) {
     const int64_t kbeg = lo_first, kend = hi_last;
 
     const float *Q = static_cast<const float *>(p.q) + ((int64_t)b * p.H + h) * Nq * D;
-    const float *K = static_cast<const float *>(p.k) + ((int64_t)b * p.Hkv + g) * Nk * D;
-    const float *V = static_cast<const float *>(p.v) + ((int64_t)b * p.Hkv + g) * Nk * D;
+    const float *K = static_cast<const float *>(p.k) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
+    const float *V = static_cast<const float *>(p.v) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
 
     f32x4 qv[DC], acc[DC];
 #pragma unroll

@@ -15,6 +15,10 @@ int launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream);
 int launch_splitkv_decode(const FwdParams &p, int d, hipStream_t stream);
 // Rows of query rows per K/V head up to which the decode kernel is used.
 int splitkv_decode_max_rows();
+// Write rows of T tokens starting at pos into a rolling cache (sink rows,
+// then a ring of window slots); n_rows = B * Hkv * T.
+int launch_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache, int64_t n_rows, int64_t T,
+                     int64_t pos, int64_t window, int64_t sinks, int d, hipStream_t stream);
 // Merge per-split partials into O (bf16 or fp32) and lse.
 int launch_combine(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse,
                    int64_t rows, int num_splits, int d, int out_dtype, hipStream_t stream);

@@ -68,8 +68,8 @@ __global__ __launch_bounds__(NT) void splitkv_decode_kernel(const FwdParams p) {
     const int64_t s_hi = s_lo + p.split_len < Nk ? s_lo + p.split_len : Nk;
     const int GR = p.group * (int)Nq;
 
-    const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * Nk * D;
-    const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * Nk * D;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
     const float c_log2 = p.scale * kLog2e;
 
     for (int r0 = 0; r0 < GR; r0 += R) {

@@ -26,7 +26,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MAX_HEAD_WINDOWS = 256
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
+            "fa_decode_rolling", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -78,7 +79,11 @@ def load_library():
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                    f32, ci, ci, f32, ci, vp]
     lib.fa_combine.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
-    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine"):
+    lib.fa_kv_append.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp]
+    lib.fa_decode_rolling.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                      f32, f32, ci, vp]
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
+                 "fa_decode_rolling"):
         getattr(lib, name).restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -151,6 +156,20 @@ def fa_combine(o_part, m_part, l_part, o, lse, B, H, Nq, d, num_splits, out_dtyp
            "fa_combine")
 
 
+def fa_kv_append(k_new, v_new, k_cache, v_cache, B, Hkv, T, d, pos, window, sinks, stream=None):
+    _check(load_library().fa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), B, Hkv, T, d,
+                                        int(pos), int(window), int(sinks), _stream(stream)),
+           "fa_kv_append")
+
+
+def fa_decode_rolling(q, k_cache, v_cache, o_part, m_part, l_part, B, H, Hkv, d, pos, window, sinks, scale,
+                      softcap, num_splits, stream=None):
+    _check(load_library().fa_decode_rolling(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o_part), _ptr(m_part), _ptr(l_part), B, H, Hkv, d,
+        int(pos), int(window), int(sinks), float(scale), float(softcap), int(num_splits), _stream(stream)),
+        "fa_decode_rolling")
+
+
 # ------------------------------------------------------------- conveniences
 def _shapes(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -219,3 +238,51 @@ def splitkv_attention(q, k, v, num_splits, scale=None, causal=False, window=0, s
     if return_partials:
         return o, lse, (o_part, m_part, l_part)
     return o, lse
+
+
+class RollingKVCache:
+    """One layer's rolling KV cache for streaming decode: ``sinks`` rows that
+    keep the first tokens, then a ring of ``window`` rows for the most recent
+    ones (bf16 [B, Hkv, sinks + window, d] each, allocated with torch).
+    ``append`` writes the next tokens' K/V (fa_kv_append); ``attend`` runs
+    fa_decode_rolling + fa_combine for the query of the last written token."""
+
+    def __init__(self, B, Hkv, d, window, sinks=4, device="cuda"):
+        import torch
+        self.B, self.Hkv, self.d, self.window, self.sinks = int(B), int(Hkv), int(d), int(window), int(sinks)
+        shape = (self.B, self.Hkv, self.sinks + self.window, self.d)
+        self.k = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.v = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        self.length = 0  # tokens written so far (positions 0 .. length-1)
+
+    def append(self, k_new, v_new, stream=None):
+        """k_new, v_new: bf16 [B, Hkv, T, d], the tokens at positions
+        length .. length+T-1."""
+        B, Hkv, T, d = k_new.shape
+        if (B, Hkv, d) != (self.B, self.Hkv, self.d) or v_new.shape != k_new.shape:
+            raise ValueError("k_new / v_new shape does not match the cache")
+        fa_kv_append(k_new, v_new, self.k, self.v, B, Hkv, T, d, self.length, self.window, self.sinks, stream)
+        self.length += T
+
+    def attend(self, q, num_splits=4, scale=None, softcap=0.0, out_dtype=None, stream=None):
+        """Attention of q (bf16 [B, H, 1, d]), the query of the token at
+        position length-1, over the sink tokens and the window."""
+        import torch
+        if self.length < 1:
+            raise ValueError("the cache is empty")
+        B, H, Nq, d = q.shape
+        if Nq != 1 or B != self.B or d != self.d:
+            raise ValueError("q must be [B, H, 1, d] for this cache")
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        S = int(num_splits)
+        o_part = torch.empty((B, H, 1, S, d), dtype=torch.float32, device=q.device)
+        m_part = torch.empty((B, H, 1, S), dtype=torch.float32, device=q.device)
+        l_part = torch.empty((B, H, 1, S), dtype=torch.float32, device=q.device)
+        out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+        o = torch.empty((B, H, 1, d), dtype=out_dtype, device=q.device)
+        lse = torch.empty((B, H, 1), dtype=torch.float32, device=q.device)
+        fa_decode_rolling(q, self.k, self.v, o_part, m_part, l_part, B, H, self.Hkv, d, self.length - 1,
+                          self.window, self.sinks, scale, softcap, S, stream)
+        fa_combine(o_part, m_part, l_part, o, lse, B, H, 1, d, S,
+                   FA_DTYPE_BF16 if out_dtype == torch.bfloat16 else FA_DTYPE_FP32, stream)
+        return o, lse

@@ -84,6 +84,51 @@ WORKLOADS = {
     ]
 }
 
+
+
+@dataclass(frozen=True)
+class RollingWorkload:
+    """Streaming decode over a rolling KV cache (Transformers & Math 16.3
+    window, 16.6 attention sinks): B sequences, each at position ``pos``,
+    one query token per sequence, a cache of ``sinks + window`` rows per
+    (sequence, K/V head)."""
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    d: int
+    window: int
+    sinks: int
+    pos: int
+    num_splits: int
+    seed: int
+    scale: float = 0.0
+
+    @property
+    def rows(self) -> int:
+        """Filled cache rows: the sink tokens and the window."""
+        return min(self.pos + 1, self.sinks + self.window)
+
+
+# Streaming decode at the pages' window (4096) with 4 sink tokens, on the
+# split-KV decode workload's batch and head shape, far into the stream.
+ROLLING = RollingWorkload("bf16_rolling_decode_b16_h32kv8_w4096_s4_d128", 16, 32, 8, 128, 4096, 4, 65535, 4,
+                          seed=6, scale=1.0 / math.sqrt(128))
+
+
+def rolling_bytes(w: RollingWorkload) -> int:
+    """Bytes one streaming step must move: the new token's K and V read and
+    written into the cache, every filled cache row of K and V read once, Q
+    read, O and lse written, and the fp32 partials written and read."""
+    kv_row = w.B * w.Hkv * w.d * 2
+    append = 2 * 2 * kv_row
+    cache = 2 * w.rows * kv_row
+    q = o = w.B * w.H * w.d * 2
+    lse = w.B * w.H * 4
+    part = w.B * w.H * w.num_splits * (w.d + 2) * 4
+    return append + cache + q + o + lse + 2 * part
+
+
 # The order in which the workloads are listed above; index 0 is the small
 # case, index 2 the causal prefill the prefill throughput is quoted on.
 ORDER = list(WORKLOADS)

@@ -128,3 +128,30 @@ def test_fwd_ex_validation():
     a2 = fa.FwdArgs(fa.FA_DTYPE_BF16, FAKE, FAKE, FAKE, FAKE, None, 1, 512, 512, 8, 8, 64, 0.1, 1, 0, 0.0,
                     ctypes.cast(big, ctypes.POINTER(ctypes.c_int32)), FAKE)
     assert lib.fa_fwd_ex(ctypes.byref(a2)) == fa.FA_ERR_UNSUPPORTED         # H > FA_MAX_HEAD_WINDOWS
+
+
+def test_rolling_cache_validation():
+    # every rejected call returns before any launch, so it runs without a GPU
+    lib = fa.load_library()
+    app = [FAKE, FAKE, FAKE, FAKE, 2, 2, 3, 64]           # k_new, v_new, k_cache, v_cache, B, Hkv, T, d
+    assert lib.fa_kv_append(*app, -1, 8, 4, FAKE) == fa.FA_ERR_INVALID_ARG      # pos < 0
+    assert lib.fa_kv_append(*app, 5, 0, 4, FAKE) == fa.FA_ERR_INVALID_ARG       # window < 1
+    assert lib.fa_kv_append(*app, 5, 8, -1, FAKE) == fa.FA_ERR_INVALID_ARG      # sinks < 0
+    a2 = list(app); a2[2] = None
+    assert lib.fa_kv_append(*a2, 5, 8, 4, FAKE) == fa.FA_ERR_INVALID_ARG        # NULL cache
+    a3 = list(app); a3[7] = 80
+    assert lib.fa_kv_append(*a3, 5, 8, 4, FAKE) == fa.FA_ERR_UNSUPPORTED        # d = 80
+    a4 = list(app); a4[6] = 0; a4[0] = a4[1] = a4[2] = a4[3] = None
+    assert lib.fa_kv_append(*a4, 5, 8, 4, FAKE) == fa.FA_OK                     # no tokens: no-op
+    dec = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64]  # q, caches, partials, B, H, Hkv, d
+    assert lib.fa_decode_rolling(*dec, 10, 8, 4, 0.1, 0.0, 0, FAKE) == fa.FA_ERR_INVALID_ARG   # num_splits
+    assert lib.fa_decode_rolling(*dec, -2, 8, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG   # pos
+    assert lib.fa_decode_rolling(*dec, 10, 0, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG   # window
+    d2 = list(dec); d2[7] = 3
+    assert lib.fa_decode_rolling(*d2, 10, 8, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG    # H % Hkv
+    d3 = list(dec); d3[4] = None
+    assert lib.fa_decode_rolling(*d3, 10, 8, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG    # NULL m_part
+    assert lib.fa_decode_rolling(*dec, 10, 8, 4, float("nan"), 0.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_decode_rolling(*dec, 10, 8, 4, 0.1, -2.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG
+    d4 = list(dec); d4[9] = 96
+    assert lib.fa_decode_rolling(*d4, 10, 8, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_UNSUPPORTED
