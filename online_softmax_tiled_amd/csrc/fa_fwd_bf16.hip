@@ -63,6 +63,9 @@ constexpr int BN = 64;            // keys per tile
 constexpr int NT = 64 * NW;       // threads per workgroup
 constexpr int LOADERS = 4;        // waves that issue the tile loads
 constexpr float TAU = 8.0f;       // lazy-rescale threshold, log2 units
+// Largest soft-cap for the fixed reference maximum: e^60 per weight leaves
+// room for 2^31 keys below the fp32 maximum (3.4e38).
+constexpr float kFixedMaxCap = 60.0f;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -206,12 +209,13 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
 }
 
 // Per-wave state and the pieces of one pipelined step.
-template <int D, bool EXPLICIT, bool CAP>
+template <int D, bool EXPLICIT, bool CAP, bool FIXED>
 struct Wave {
     using L = Smem<D>;
     bf16x8 qf[RB][D / 16];      // Q^T operand, per row block
     f32x16 oacc[RB][D / 32];    // O^T accumulators
     float m[RB], l[RB];         // lazy reference max (log2 units); this lane's half of the sum
+    float lx[RB];               // FIXED: this lane's half of the sum of the fp32 weights (for lse)
     float mtrue[RB];            // exact running max (log2 units)
     int lo_rel[RB], hi_rel[RB]; // visible keys relative to the first tile
     int koff[D / 16];           // K operand read offsets (bytes)
@@ -244,7 +248,10 @@ struct Wave {
 
     // Online softmax of one tile: masks (if MASK), row max, lazy move of the
     // reference maximum (branch-free; returns whether any row moved and the
-    // factors), weights rounded to bf16 as the P^T operand.
+    // factors), weights rounded to bf16 as the P^T operand.  FIXED (soft-
+    // capped scores, |z| <= softcap <= kFixedMaxCap): the reference maximum
+    // stays 0, every weight e^z lies in [e^-cap, e^cap], inside fp32 and
+    // bf16 range, and the row maximum, the move and the rescale are skipped.
     template <bool MASK>
     __device__ __forceinline__ bool softmax(f32x16 (&sacc)[RB][2], int it, bf16x8 (&pf)[RB][4],
                                             float (&alpha)[RB]) {
@@ -272,6 +279,7 @@ struct Wave {
                         if (!((uint32_t)(c - base) < span)) sacc[r][kb][j] = kNegInf;
                     }
             }
+            if (FIXED) continue;
             float x = sacc[r][0][0];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -280,6 +288,38 @@ struct Wave {
             mt[r] = EXPLICIT ? x : x * c_log2;
             mt[r] = row_max(mt[r]);
             mtrue[r] = fmaxf(mtrue[r], mt[r]);
+        }
+        if (FIXED) {
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                alpha[r] = 1.0f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) sacc[r][kb][j] = fast_exp2(sacc[r][kb][j]);
+                // O is normalised by the sum of the same bf16 weights P.V uses
+                // (pv), so it stays a convex combination of V rows; lse takes
+                // the sum of the fp32 weights: with no running maximum no
+                // weight is exactly 1, and the bf16 rounding of a dominant
+                // weight would otherwise reach lse.
+                float rs[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rs[i] = (sacc[r][i / 4][4 * (i % 4)] + sacc[r][i / 4][4 * (i % 4) + 1]) +
+                            (sacc[r][i / 4][4 * (i % 4) + 2] + sacc[r][i / 4][4 * (i % 4) + 3]);
+                lx[r] += ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int gp = 0; gp < 2; ++gp) {
+                        u32x4 xq;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            xq[e] = pack_bf16x2(sacc[r][kb][8 * gp + 2 * e], sacc[r][kb][8 * gp + 2 * e + 1]);
+                        pf[r][kb * 2 + gp] = __builtin_bit_cast(bf16x8, xq);
+                    }
+            }
+            return false;
         }
         bool grow = false;
 #pragma unroll
@@ -363,7 +403,7 @@ struct Wave {
     }
 };
 
-template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
+template <int D, bool SPLIT, bool EXPLICIT, bool CAP, bool FIXED>
 __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, const int n_qtiles) {
     using L = Smem<D>;
     // Separate arrays per buffer so the compiler can tell the buffer being
@@ -408,7 +448,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + ((int64_t)b * p.Hkv + g) * p.kv_rows * D;
 
-    Wave<D, EXPLICIT, CAP> st;
+    Wave<D, EXPLICIT, CAP, FIXED> st;
     st.hf = hf;
     st.c_log2 = p.scale * kLog2e;
     st.scale = p.scale;
@@ -428,9 +468,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
             if (qrow < Nq) x = ldg16(Q + qrow * D + ds * 16 + hf * 8);
             st.qf[0][ds] = __builtin_bit_cast(bf16x8, x);
         }
-        st.m[0] = kNegInf;
+        st.m[0] = FIXED ? 0.0f : kNegInf;
         st.mtrue[0] = kNegInf;
         st.l[0] = 0.0f;
+        st.lx[0] = 0.0f;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -553,6 +594,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
 
     // ---- epilogue: O = acc / l.  Lane holds dims db*32 + 8*(j/4) + 4*hf + (j%4).
     const float lr = row_sum(st.l[0]);  // both halves of the row
+    const float ls = FIXED ? row_sum(st.lx[0]) : lr;  // the sum lse is taken from
     if (qrow >= Nq) return;
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     const int64_t row = ((int64_t)b * p.H + h) * Nq + qrow;
@@ -566,7 +608,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
                            pack_bf16x2(st.oacc[0][db][4 * gq + 2] * inv, st.oacc[0][db][4 * gq + 3] * inv)};
                 *reinterpret_cast<u32x2 *>(O + db * 32 + 8 * gq + 4 * hf) = x;
             }
-        if (p.lse && hf == 0) p.lse[row] = lr > 0.0f ? (st.m[0] + __log2f(lr)) * kLn2 : kNegInf;
+        if (p.lse && hf == 0) p.lse[row] = ls > 0.0f ? (st.m[0] + __log2f(ls)) * kLn2 : kNegInf;
     } else {
         const int64_t prow = row * p.num_splits + w.split;
         float *Op = p.o_part + prow * D;
@@ -586,20 +628,26 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
     }
 }
 
-template <int D, bool SPLIT, bool EXPLICIT, bool CAP>
+template <int D, bool SPLIT, bool EXPLICIT, bool CAP, bool FIXED = false>
 int launch_one(const FwdParams &p, hipStream_t stream) {
     const int n_qtiles = (int)((p.Nq + BM - 1) / BM);
     const int64_t blocks = p.B * p.H * (int64_t)n_qtiles * p.num_splits;
     if (blocks <= 0) return FA_OK;
     if (blocks > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, SPLIT, EXPLICIT, CAP>), dim3((unsigned)blocks), dim3(NT), 0, stream, p,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, SPLIT, EXPLICIT, CAP, FIXED>), dim3((unsigned)blocks), dim3(NT), 0, stream, p,
                        n_qtiles);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 template <int D, bool SPLIT>
 int launch_s(const FwdParams &p, hipStream_t stream) {
-    if (p.softcap > 0.0f) return launch_one<D, SPLIT, true, true>(p, stream);
+    if (p.softcap > 0.0f) {
+        // Soft-capped scores are bounded by the cap: a fixed reference
+        // maximum replaces the running one (split partials keep their exact
+        // maxima, so only the unsplit pass uses it).
+        if (!SPLIT && p.softcap <= kFixedMaxCap) return launch_one<D, false, true, true, true>(p, stream);
+        return launch_one<D, SPLIT, true, true>(p, stream);
+    }
     if (!(p.scale > 0.0f)) return launch_one<D, SPLIT, true, false>(p, stream);
     return launch_one<D, SPLIT, false, false>(p, stream);
 }

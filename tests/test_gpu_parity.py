@@ -344,3 +344,19 @@ def test_gpu_rejects_bad_arguments():
     with pytest.raises(fa.FaError) as e:
         fa.attention(q, k, k)
     assert e.value.status == -2
+
+
+# Soft-capped scores are bounded by the cap, so up to a cap of 60 the kernel
+# keeps a fixed reference maximum of 0 (no running maximum, no rescale);
+# above it the running maximum is used.  Both must give the exact result,
+# also with the scores saturated near +-cap: Q and K are scaled by 3 (scores
+# reach a few hundred before the cap), V keeps the workloads' N(0, 1) values
+# the absolute O tolerance is set for.
+@pytest.mark.parametrize("cap", [1.0, 50.0, 60.0, 61.0, 200.0])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_softcap_fixed_and_running_maximum(cap, d):
+    print(f"case softcap cap={cap} d={d}", flush=True)
+    inp = rand_inputs(2, 4, 2, 200, 333, d, seed=int(cap) + d, dtype="bf16")
+    inp["q"], inp["k"] = (wl.round_bf16(inp[n] * np.float32(3.0)) for n in ("q", "k"))
+    parity(inp, "bf16", 1.0, causal=True, softcap=cap, what=f"cap={cap}")
+    parity(inp, "bf16", 1.0 / math.sqrt(d), causal=True, window=50, softcap=cap, what=f"cap={cap} window")
