@@ -164,7 +164,7 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part,
  * Rolling KV cache with attention sinks, for streaming decode.
  *
  * Transformers & Math section 16.3: a local (sliding-window) layer attends
- * to the W most recent tokens only, so its cache never holds more than W
+ * to the last W positions only, so its cache never needs more than W
  * entries; section 16.6: streaming keeps the first few tokens (attention
  * sinks, 4 in the setup it describes) alongside the window.  A cache of one
  * such layer is two bf16 tensors k_cache, v_cache [B, Hkv, sinks + window, d]
@@ -173,7 +173,7 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part,
  * token t >= sinks lives in row sinks + (t - sinks) % window until token
  * t + window replaces it.  After tokens 0 .. pos were written, the filled
  * rows are the prefix [0, min(pos + 1, sinks + window)) and hold exactly the
- * sink tokens and the window of the W most recent tokens.
+ * sink tokens and the window of the last W positions.
  */
 
 /*
@@ -200,7 +200,7 @@ int fa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_ca
  * fa_fwd_splitkv with Nq = 1 (o_part [B,H,1,S,d], m_part and l_part
  * [B,H,1,S], fp32); fa_combine(..., Nq = 1, ...) then gives the output and
  * lse.  The result is attention of that query over the sink tokens and the
- * window of the W most recent tokens, each once.  scale and softcap as
+ * window of the last W positions, each once.  scale and softcap as
  * fa_fwd.  Errors as fa_kv_append, plus FA_ERR_INVALID_ARG for
  * num_splits < 1, H % Hkv != 0, non-finite scale or softcap < 0.
  */

@@ -1,7 +1,7 @@
 // fa_cache.hip -- writes tokens into a rolling KV cache for streaming
 // decode: rows [0, sinks) keep the first tokens for good (attention sinks,
 // Transformers & Math section 16.6) and rows [sinks, sinks + window) are a
-// ring holding the window of the most recent tokens (section 16.3: a local
+// ring holding the window of the latest tokens (section 16.3: a local
 // layer's cache never exceeds its window).
 //
 // Token t goes to row t when t < sinks, else to row sinks + (t - sinks) %

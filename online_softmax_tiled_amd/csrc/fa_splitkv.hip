@@ -6,7 +6,7 @@
 // the chunk's normalised output.  fa_combine merges them with the two-block
 // rule of Transformers & Math, Module 16, section 16.2 (l = e^(m1-m) l1 +
 // e^(m2-m) l2, outputs weighted by their share of l), applied to all splits
-// at once ("more blocks repeat the same update").
+// at once (folding further blocks in one by one gives the same result).
 //
 // Decode kernel (few query rows per K/V head; HBM-bound, 4 FLOP per byte):
 //   * one workgroup per (batch, K/V head, split); all query heads of the

@@ -23,7 +23,7 @@
  *     an empty result and a zero normaliser leaves the output at zero.
  *   - Transformers & Math, Module 16: section 16.5 (soft-cap
  *     kappa*tanh(z/kappa) applied to z = QK^T/sqrt(d_k)), section 16.3
- *     (sliding window: the W most recent tokens), section 16.2 "Measured"
+ *     (sliding window: a query sees only the last W positions), section 16.2 "Measured"
  *     (causal mask by absolute position in the full sequence) and the two
  *     merge equations of section 16.2 for combining per-block (m, l, O).
  *
@@ -32,7 +32,7 @@
  *     query aligned with the last key); causal keeps j <= p;
  *   - a window W > 0 keeps p - W < j, i.e. exactly W keys including the
  *     query's own position; it is defined only together with causal;
- *   - attention sinks (section 16.6, streaming: the first 4 tokens are
+ *   - attention sinks (section 16.6, streaming: the opening tokens are
  *     always kept alongside the sliding window): with sinks = S > 0 the
  *     keys j < S stay visible to a windowed row whatever its window (still
  *     subject to the causal rule j <= p);
@@ -263,7 +263,7 @@ int oracle_attention(const double *q, const double *k, const double *v,
  * Follows the two merge equations of Transformers & Math section 16.2: with
  * m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2 and
  * O = (e^(m1-m) l1 / l) O1 + (e^(m2-m) l2 / l) O2, where O_i is block i's own
- * normalised output; more blocks repeat the same update against the running
+ * normalised output; further blocks are folded in one at a time against the running
  * result, here in block order s = 0, 1, ..., S-1.  A block with l_s = 0 saw
  * no visible key and carries no weight; it is skipped.
  *

@@ -4,7 +4,7 @@ fa_combine) against the fp64 oracle.
 A stream of tokens is written into the cache (a chunk, then one token at a
 time); at chosen positions the decode query attends to the cache and must
 match the oracle's attention over the whole sequence with the causal rule,
-a window of the W most recent tokens and the first `sinks` tokens kept
+a window of the last W positions and the first `sinks` tokens kept
 (Transformers & Math 16.3 and 16.6).  The cache contents are byte copies
 and are compared exactly with the ring rule.  bf16 tolerances as in
 test_gpu_parity.
