@@ -15,7 +15,9 @@ A step is one forward pass over one batch of synthetic input:
 * rolling (same condition): streaming decode over a rolling KV cache with
   attention sinks -- ``fa_kv_append`` of one token + ``fa_decode_rolling``
   + ``fa_combine`` (B=16, H=32, Hkv=8, d=128, window 4096, 4 sinks, 4
-  splits, position 65535), in GB/s.
+  splits, position 65535), in GB/s;
+* softmax (same condition): ``fa_softmax`` (online normaliser) and
+  ``fa_softmax_topk`` (k = 8) on 512 rows of 256000 fp32 logits, in GB/s.
 
 Inputs are seeded synthetic tensors (online_softmax_tiled_amd.workloads),
 resident in HBM before timing starts.  Kernel durations are taken with HIP
@@ -201,6 +203,34 @@ def bench_rolling(torch, fa, steps, warmup):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "splitkv_decode_kernel (rolling cache)", "avg_ms": round(avg_dec, 4)},
     }
+
+
+def bench_softmax(torch, fa, steps, warmup):
+    """Row softmax with the online normaliser and the fused softmax top-k on
+    vocabulary-sized rows (fp32)."""
+    w = wl.SOFTMAX
+    rng = np.random.default_rng(w.seed)
+    x = torch.from_numpy((rng.standard_normal((w.rows, w.n)) * 3.0).astype(np.float32)).cuda()
+    y = torch.empty_like(x)
+    probs = torch.empty((w.rows, w.k), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.rows, w.k), dtype=torch.int32, device="cuda")
+
+    def sm():
+        fa.fa_softmax(x, y, None, w.rows, w.n, fa.fa.FA_DTYPE_FP32)
+
+    def tk():
+        fa.fa_softmax_topk(x, probs, idx, None, w.rows, w.n, w.k, fa.fa.FA_DTYPE_FP32)
+
+    b = wl.softmax_bytes(w)
+    out = {"workload": w.name, "config": {"rows": w.rows, "n": w.n, "k": w.k, "dtype": "fp32"}}
+    for name, fn, nbytes in (("softmax", sm, b["softmax_online"]), ("topk", tk, b["topk_fused"])):
+        avg, total, _ = time_launches(fn, steps, warmup, torch)
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        out[name] = {"ms_per_step": round(avg, 4), "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    out["softmax"]["bytes_note"] = "two reads of x and one write of y (online normaliser)"
+    out["topk"]["bytes_note"] = "one read of x; k probabilities and indices written"
+    return out
 
 
 def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
@@ -417,7 +447,7 @@ def main():
     torch.cuda.init()
 
     main_w, leg = None, None
-    decode = rolling = None
+    decode = rolling = softmax = None
     if args.workload == "prefill":
         main_w, leg = bench_prefill(torch, fa, args.steps, args.warmup)
         print(f"[bench] prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
@@ -427,6 +457,9 @@ def main():
             rolling = bench_rolling(torch, fa, args.steps, args.warmup)
             print(f"[bench] rolling decode done: {rolling['ms_per_step']:.4f} ms/step", file=sys.stderr,
                   flush=True)
+            softmax = bench_softmax(torch, fa, args.steps, args.warmup)
+            print(f"[bench] softmax done: {softmax['softmax']['ms_per_step']:.4f} ms, top-k "
+                  f"{softmax['topk']['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
         value, unit = leg["value"], "TFLOP/s"
     else:
         main_w, leg = bench_decode(torch, fa, args.steps, args.warmup)
@@ -450,6 +483,8 @@ def main():
                          "roofline": decode["roofline"]}
     if rolling is not None:
         out["rolling"] = rolling
+    if softmax is not None:
+        out["softmax"] = softmax
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)

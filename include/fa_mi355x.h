@@ -210,6 +210,40 @@ int fa_decode_rolling(const void *q, const void *k_cache, const void *v_cache,
                       int64_t pos, int64_t window, int64_t sinks,
                       float scale, float softcap, int num_splits, fa_stream_t stream);
 
+/*
+ * Row softmax with the online normaliser ("Online normalizer calculation
+ * for softmax", abstract: the classical softmax with fewer memory passes;
+ * the notebook "Online Softmax Without the Attention Matrix": the running
+ * maximum and denominator recurrence).
+ *
+ * fa_softmax -- y[r, j] = exp(x[r, j] - max_j x[r, :]) / sum_j exp(...) for
+ * each of `rows` rows of n values; lse[r] = max + ln sum (fp32, or NULL).
+ * x, y: device, row-major [rows, n], both fp32 (FA_DTYPE_FP32) or both bf16
+ * (FA_DTYPE_BF16, y rounded to nearest even); fp32 arithmetic.  The maximum
+ * and the normaliser come from one read of each row; a second read writes y.
+ * Rows need at least one finite value (NaN or +inf inputs are undefined).
+ * Errors: FA_ERR_INVALID_ARG for negative sizes, an unknown dtype or NULL
+ * x / y when rows*n > 0; FA_ERR_UNSUPPORTED for rows >= 2^31.
+ */
+int fa_softmax(const void *x, void *y, float *lse, int64_t rows, int64_t n, int dtype,
+               fa_stream_t stream);
+
+/* Largest k supported by fa_softmax_topk. */
+#define FA_MAX_TOPK 64
+
+/*
+ * fa_softmax_topk -- the k largest softmax probabilities of each row and
+ * their column indices, from ONE read of x: the online normaliser and a
+ * running top-k are kept together.  probs: fp32 [rows, k] in descending
+ * order; indices: int32 [rows, k]; equal values come lower column first.
+ * lse as fa_softmax (or NULL).  1 <= k <= min(n, FA_MAX_TOPK).
+ * Errors: FA_ERR_INVALID_ARG for negative sizes, k out of range, an unknown
+ * dtype or NULL x / probs / indices when rows > 0; FA_ERR_UNSUPPORTED for
+ * rows or n >= 2^31.
+ */
+int fa_softmax_topk(const void *x, float *probs, int32_t *indices, float *lse, int64_t rows,
+                    int64_t n, int k, int dtype, fa_stream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *fa_status_string(int status);
 

@@ -15,8 +15,12 @@ from .fa import (  # noqa: F401
     fa_fwd_f32,
     fa_fwd_splitkv,
     fa_kv_append,
+    fa_softmax,
+    fa_softmax_topk,
     fa_status_string,
     library_path,
     load_library,
+    softmax,
+    softmax_topk,
     splitkv_attention,
 )

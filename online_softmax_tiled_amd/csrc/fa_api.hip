@@ -204,6 +204,23 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part, vo
                               reinterpret_cast<hipStream_t>(stream));
 }
 
+int fa_softmax(const void *x, void *y, float *lse, int64_t rows, int64_t n, int dtype, fa_stream_t stream) {
+    if (rows < 0 || n < 0) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
+    if (rows > 0 && n > 0 && (!x || !y)) return FA_ERR_INVALID_ARG;
+    if (rows > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    return fa::launch_softmax(x, y, lse, rows, n, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+int fa_softmax_topk(const void *x, float *probs, int32_t *indices, float *lse, int64_t rows, int64_t n, int k,
+                    int dtype, fa_stream_t stream) {
+    if (rows < 0 || n < 0 || k < 1 || k > FA_MAX_TOPK) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
+    if (rows > 0 && (k > n || !x || !probs || !indices)) return FA_ERR_INVALID_ARG;
+    if (rows > 0x7fffffff || n > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    return fa::launch_softmax_topk(x, probs, indices, lse, rows, n, k, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
 const char *fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";

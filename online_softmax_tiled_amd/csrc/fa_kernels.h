@@ -19,6 +19,10 @@ int splitkv_decode_max_rows();
 // then a ring of window slots); n_rows = B * Hkv * T.
 int launch_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache, int64_t n_rows, int64_t T,
                      int64_t pos, int64_t window, int64_t sinks, int d, hipStream_t stream);
+// Row softmax (online normaliser) and its fused top-k.
+int launch_softmax(const void *x, void *y, float *lse, int64_t rows, int64_t n, int dtype, hipStream_t stream);
+int launch_softmax_topk(const void *x, float *probs, int32_t *idx, float *lse, int64_t rows, int64_t n, int k,
+                        int dtype, hipStream_t stream);
 // Merge per-split partials into O (bf16 or fp32) and lse.
 int launch_combine(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse,
                    int64_t rows, int num_splits, int d, int out_dtype, hipStream_t stream);

@@ -27,7 +27,8 @@ FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MAX_HEAD_WINDOWS = 256
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
-            "fa_decode_rolling", "fa_status_string")
+            "fa_decode_rolling", "fa_softmax", "fa_softmax_topk", "fa_status_string")
+FA_MAX_TOPK = 64
 
 
 class FaError(RuntimeError):
@@ -82,8 +83,10 @@ def load_library():
     lib.fa_kv_append.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, vp]
     lib.fa_decode_rolling.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                       f32, f32, ci, vp]
+    lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, ci, vp]
+    lib.fa_softmax_topk.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
-                 "fa_decode_rolling"):
+                 "fa_decode_rolling", "fa_softmax", "fa_softmax_topk"):
         getattr(lib, name).restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -168,6 +171,17 @@ def fa_decode_rolling(q, k_cache, v_cache, o_part, m_part, l_part, B, H, Hkv, d,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o_part), _ptr(m_part), _ptr(l_part), B, H, Hkv, d,
         int(pos), int(window), int(sinks), float(scale), float(softcap), int(num_splits), _stream(stream)),
         "fa_decode_rolling")
+
+
+def fa_softmax(x, y, lse, rows, n, dtype, stream=None):
+    _check(load_library().fa_softmax(_ptr(x), _ptr(y), _ptr(lse), rows, n, int(dtype), _stream(stream)),
+           "fa_softmax")
+
+
+def fa_softmax_topk(x, probs, indices, lse, rows, n, k, dtype, stream=None):
+    _check(load_library().fa_softmax_topk(_ptr(x), _ptr(probs), _ptr(indices), _ptr(lse), rows, n, int(k),
+                                           int(dtype), _stream(stream)),
+           "fa_softmax_topk")
 
 
 # ------------------------------------------------------------- conveniences
@@ -286,3 +300,36 @@ class RollingKVCache:
         fa_combine(o_part, m_part, l_part, o, lse, B, H, 1, d, S,
                    FA_DTYPE_BF16 if out_dtype == torch.bfloat16 else FA_DTYPE_FP32, stream)
         return o, lse
+
+
+def _rows_dtype(x):
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 or bf16 CUDA tensor")
+    n = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // n if n else 0
+    return rows, n, FA_DTYPE_BF16 if x.dtype == torch.bfloat16 else FA_DTYPE_FP32
+
+
+def softmax(x, return_lse=False, stream=None):
+    """Softmax over the last axis of x (fp32 or bf16, same dtype out) with the
+    online normaliser (fa_softmax)."""
+    import torch
+    rows, n, dt = _rows_dtype(x)
+    y = torch.empty_like(x)
+    lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if return_lse else None
+    fa_softmax(x, y, lse, rows, n, dt, stream)
+    return (y, lse) if return_lse else y
+
+
+def softmax_topk(x, k, return_lse=False, stream=None):
+    """The k largest softmax probabilities over the last axis of x and their
+    indices (descending; equal values lower index first), from one read of x
+    (fa_softmax_topk).  Returns (probs fp32 [..., k], indices int32 [..., k])."""
+    import torch
+    rows, n, dt = _rows_dtype(x)
+    probs = torch.empty(x.shape[:-1] + (k,), dtype=torch.float32, device=x.device)
+    idx = torch.empty(x.shape[:-1] + (k,), dtype=torch.int32, device=x.device)
+    lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if return_lse else None
+    fa_softmax_topk(x, probs, idx, lse, rows, n, k, dt, stream)
+    return (probs, idx, lse) if return_lse else (probs, idx)

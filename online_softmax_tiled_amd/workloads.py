@@ -129,6 +129,32 @@ def rolling_bytes(w: RollingWorkload) -> int:
     return append + cache + q + o + lse + 2 * part
 
 
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    """Row softmax over a vocabulary-sized axis: ``rows`` rows of ``n`` fp32
+    logits, and the ``k`` largest probabilities of each row."""
+    name: str
+    rows: int
+    n: int
+    k: int
+    seed: int
+
+
+# The first Gemma's 256,000-token vocabulary (Transformers & Math 16.3), 512
+# rows of logits: 1 MB per row, more than a CU's LDS, so the online
+# normaliser's two reads are the minimum for the full softmax.
+SOFTMAX = SoftmaxWorkload("fp32_softmax_rows512_n256000", 512, 256000, 8, seed=7)
+
+
+def softmax_bytes(w: SoftmaxWorkload) -> dict:
+    """Bytes each pass structure must move: the online softmax reads x twice
+    and writes y once (the safe three-pass softmax reads it three times); the
+    fused top-k reads x once and writes k (probability, index) pairs."""
+    x = w.rows * w.n * 4
+    return {"softmax_online": 2 * x + x + w.rows * 4, "softmax_three_pass": 3 * x + x + w.rows * 4,
+            "topk_fused": x + w.rows * w.k * 8 + w.rows * 4}
+
+
 # The order in which the workloads are listed above; index 0 is the small
 # case, index 2 the causal prefill the prefill throughput is quoted on.
 ORDER = list(WORKLOADS)

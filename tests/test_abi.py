@@ -155,3 +155,25 @@ def test_rolling_cache_validation():
     assert lib.fa_decode_rolling(*dec, 10, 8, 4, 0.1, -2.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG
     d4 = list(dec); d4[9] = 96
     assert lib.fa_decode_rolling(*d4, 10, 8, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_softmax_validation():
+    lib = fa.load_library()
+    F, B = fa.FA_DTYPE_FP32, fa.FA_DTYPE_BF16
+    assert lib.fa_softmax(FAKE, FAKE, None, -1, 8, F, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_softmax(FAKE, FAKE, None, 4, -8, F, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_softmax(FAKE, FAKE, None, 4, 8, 9, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_softmax(None, FAKE, None, 4, 8, B, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_softmax(FAKE, None, None, 4, 8, B, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_softmax(None, None, None, 0, 8, F, FAKE) == fa.FA_OK          # no rows: no-op
+    assert lib.fa_softmax(FAKE, FAKE, None, 1 << 31, 8, F, FAKE) == fa.FA_ERR_UNSUPPORTED
+    t = [FAKE, FAKE, FAKE, None, 4, 100]
+    assert lib.fa_softmax_topk(*t, 0, F, FAKE) == fa.FA_ERR_INVALID_ARG        # k < 1
+    assert lib.fa_softmax_topk(*t, fa.FA_MAX_TOPK + 1, F, FAKE) == fa.FA_ERR_INVALID_ARG
+    t2 = list(t); t2[5] = 5
+    assert lib.fa_softmax_topk(*t2, 6, F, FAKE) == fa.FA_ERR_INVALID_ARG       # k > n
+    t3 = list(t); t3[2] = None
+    assert lib.fa_softmax_topk(*t3, 4, F, FAKE) == fa.FA_ERR_INVALID_ARG       # NULL indices
+    assert lib.fa_softmax_topk(*t, 4, 7, FAKE) == fa.FA_ERR_INVALID_ARG        # unknown dtype
+    t4 = list(t); t4[5] = 1 << 31
+    assert lib.fa_softmax_topk(*t4, 4, B, FAKE) == fa.FA_ERR_UNSUPPORTED
