@@ -266,19 +266,27 @@ def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
 
 
 # rocprofv3 runs whose output --summarize-profiles reads (DIR = their -d root).
+# The prefill and decode kernels are profiled in runs of their own legs
+# (the rolling-cache leg launches the same decode kernel at another shape).
 PROFILE_RUNS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o run -- "
-             "python bench.py --no-cpu-baseline",
-    "FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE -o run -- "
-                  "python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-    "WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE -o run -- "
-                  "python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "trace_prefill": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_prefill -o run -- "
+                     "python bench.py --no-cpu-baseline --no-decode",
+    "trace_decode": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_decode -o run -- "
+                    "python bench.py --no-cpu-baseline --workload decode",
+    "FETCH_SIZE_prefill": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE_prefill -o run -- "
+                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-decode",
+    "WRITE_SIZE_prefill": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_prefill -o run -- "
+                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-decode",
+    "FETCH_SIZE_decode": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE_decode -o run -- "
+                         "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload decode",
+    "WRITE_SIZE_decode": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_decode -o run -- "
+                         "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload decode",
     "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_FETCH_SIZE -o run -- "
                        "python bench.py --copy-calibration",
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
                        "python bench.py --copy-calibration",
 }
-KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
+KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
            "combine": "combine_kernel<128>", "copy": "__amd_rocclr_copyBuffer"}
 
 
@@ -307,9 +315,10 @@ def summarize_profiles(d):
     """Write profiles/hbm_traffic.json and the two kernel-trace summaries
     from the rocprofv3 output under d (the runs in PROFILE_RUNS)."""
     cmds = {k: v.format(d=d) for k, v in PROFILE_RUNS.items()}
-    stats = {r["Name"]: r for r in _csv(os.path.join(d, "trace", "*kernel_stats.csv"))}
+    leg = {"prefill": "prefill", "decode": "decode", "combine": "decode"}
 
-    def stat(kernel):
+    def stat(kernel, run):
+        stats = {r["Name"]: r for r in _csv(os.path.join(d, run, "*kernel_stats.csv"))}
         for name, r in stats.items():
             if kernel in name:
                 return name.replace("void fa::(anonymous namespace)::", ""), int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, \
@@ -325,13 +334,14 @@ def summarize_profiles(d):
                 "mean over dispatches), each scaled by what the same counter reads for a 1 GiB device copy "
                 "(__amd_rocclr_copyBuffer).  bench.py reports these only while source_hash matches the "
                 "kernel sources.  Written by: python bench.py --summarize-profiles DIR.",
-        "commands": [cmds[k] for k in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
+        "commands": [cmds[k] for k in ("FETCH_SIZE_prefill", "WRITE_SIZE_prefill", "FETCH_SIZE_decode",
+                                       "WRITE_SIZE_decode", "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1)},
     }
     hbm = {}
     for kind in ("prefill", "decode", "combine"):
-        f = _counter_kib(d, "FETCH_SIZE", KERNELS[kind])
-        w_ = _counter_kib(d, "WRITE_SIZE", KERNELS[kind])
+        f = _counter_kib(d, "FETCH_SIZE_" + leg[kind], KERNELS[kind])
+        w_ = _counter_kib(d, "WRITE_SIZE_" + leg[kind], KERNELS[kind])
         rb, wb = f * 1024 * fs, w_ * 1024 * ws
         hbm[kind] = (rb, wb)
         rec = {"kernel": KERNELS[kind], "fetch_kib_per_dispatch": round(f, 1),
@@ -345,14 +355,14 @@ def summarize_profiles(d):
         f.write("\n")
 
     wp, wd = wl.WORKLOADS[PREFILL], wl.WORKLOADS[DECODE]
-    name, calls, avg, mn, mx = stat(KERNELS["prefill"])
+    name, calls, avg, mn, mx = stat(KERNELS["prefill"], "trace_prefill")
     flops = wl.algorithmic_flops(wp)
     rb, wb = hbm["prefill"]
     md = f"""# fwd_bf16_kernel on the causal prefill workload (B=4, H=32, Nq=Nk=4096, d=128, bf16)
 
 Command (run from the repository root on one MI355X):
 
-    {cmds["trace"]}
+    {cmds["trace_prefill"]}
 
 Kernel trace statistics (`run_kernel_stats.csv`; every dispatch of the run,
 the bench's warm-up launches included):
@@ -375,8 +385,8 @@ of K and V by the 16 query tiles of each head are served from L2 / MALL.
     with open(os.path.join(ROOT, "profiles", f"fwd_bf16_causal_b4_h32_n4096_d128.md"), "w") as f:
         f.write(md)
 
-    name, calls, avg, mn, mx = stat(KERNELS["decode"])
-    cname, ccalls, cavg, cmn, cmx = stat(KERNELS["combine"])
+    name, calls, avg, mn, mx = stat(KERNELS["decode"], "trace_decode")
+    cname, ccalls, cavg, cmn, cmx = stat(KERNELS["combine"], "trace_decode")
     S = wd.num_splits
     part_bytes = wd.B * wd.H * wd.Nq * S * (wd.d + 2) * 4
     split_bytes = wl.algorithmic_bytes(wd) - part_bytes - (wd.B * wd.H * wd.Nq * (wd.d * 2 + 4))
@@ -386,7 +396,7 @@ of K and V by the 16 query tiles of each head are served from L2 / MALL.
 
 Command (run from the repository root on one MI355X):
 
-    {cmds["trace"]}
+    {cmds["trace_decode"]}
 
 Kernel trace statistics (`run_kernel_stats.csv`; the bench runs the split
 kernel both inside split+combine steps and alone, warm-up included):
