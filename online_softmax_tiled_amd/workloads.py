@@ -25,6 +25,11 @@ Workloads (the shapes the pages and the brief describe):
   per head, B=16, 32 query heads over 8 KV heads, 32768 keys, cut into 16
   splits that are merged afterwards.
 
+fp8 workloads (``FP8_PREFILL``: the causal prefill shape with E4M3 Q, K, V)
+draw the same fp32 normals and quantise each tensor with one scale:
+descale = max|x| / 448 (E4M3's largest value) and codes = E4M3(x /
+descale), round-to-nearest-even (:func:`to_e4m3`).
+
 All tensors are row-major: Q [B,H,Nq,d], K and V [B,Hkv,Nk,d].
 """
 from __future__ import annotations
@@ -44,7 +49,7 @@ class Workload:
     Nq: int
     Nk: int
     d: int
-    dtype: str                 # "fp32" or "bf16": the tensors' storage type
+    dtype: str                 # "fp32", "bf16" or "fp8": the tensors' storage type
     causal: bool
     scale: float
     seed: int
@@ -84,6 +89,10 @@ WORKLOADS = {
     ]
 }
 
+
+# The causal prefill shape with fp8 (E4M3) Q, K, V and bf16 output.
+FP8_PREFILL = Workload("fp8_causal_b4_h32_n4096_d128", 4, 32, 32, 4096, 4096, 128, "fp8", True,
+                       1.0 / math.sqrt(128), seed=8)
 
 
 @dataclass(frozen=True)
@@ -199,6 +208,29 @@ def generate(w: Workload, seed: int | None = None) -> dict:
     return {"q": q, "k": k, "v": v}
 
 
+def to_e4m3(x: np.ndarray):
+    """(codes, descale): x quantised to OCP E4M3 bytes with one fp32 scale,
+    descale = max|x| / 448, codes = E4M3(x / descale) rounded to nearest
+    (ties to even) by torch's CPU float8_e4m3fn conversion."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+    y = np.clip(x / descale, -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, float(descale)
+
+
+def generate_fp8(w: Workload, seed: int | None = None) -> dict:
+    """E4M3 codes (uint8) of Q, K, V drawn as in :func:`generate`, and their
+    descale factors: dict(q, k, v, q_descale, k_descale, v_descale)."""
+    x = generate(w.with_(dtype="fp32"), seed)
+    out = {}
+    for n in "qkv":
+        out[n], out[n + "_descale"] = to_e4m3(x[n])
+    return out
+
+
 def fa_seed_pattern(n: int, d: int) -> dict:
     """The deterministic input pattern of nx_flashattn_scale.nx (fa_seed):
     x = (i*a + dd*b) mod m mapped to (x - floor(m/2)) / m in fp32, with
@@ -251,10 +283,10 @@ def algorithmic_bytes(w: Workload) -> int:
     """Bytes a perfect kernel must move through HBM: Q, K and V read once,
     O and the fp32 row lse written once; split-KV also writes and reads its
     fp32 partials (O_s, m_s, l_s)."""
-    es = 4 if w.dtype == "fp32" else 2
+    es = {"fp32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     q = w.B * w.H * w.Nq * w.d * es
     kv = 2 * w.B * w.Hkv * w.Nk * w.d * es
-    o = q
+    o = w.B * w.H * w.Nq * w.d * (2 if w.dtype == "fp8" else es)  # fp8 attention writes bf16
     lse = w.B * w.H * w.Nq * 4
     total = q + kv + o + lse
     if w.num_splits:
