@@ -123,6 +123,36 @@ typedef struct fa_fwd_args {
 int fa_fwd_ex(const fa_fwd_args *args);
 
 /*
+ * fa_fwd_fp8 -- forward attention on fp8 q, k, v: both products on the fp8
+ * matrix cores, the online-softmax state (maximum, normaliser, output) in
+ * fp32, bf16 output.  A low-precision variant of the same operation: the
+ * two matrix products of the loop run in a narrow format while the softmax
+ * bookkeeping stays wide (HiFA4 abstract, there with 4-bit operands on
+ * Ascend NPUs).
+ *
+ * q, k, v: bytes in the OCP 8-bit E4M3 format (1 sign bit, 4 exponent bits
+ * with bias 7, 3 mantissa bits; no infinities, 0x7f and 0xff are NaN), one
+ * byte per element, in the layouts above.  Element values are
+ * q_descale * E4M3(q byte), k_descale * E4M3(k byte), v_descale *
+ * E4M3(v byte); each descale must be finite and > 0.  The scores are
+ * scale * <q_i, k_j> of those values, computed exactly from the products of
+ * the bytes and one fp32 factor.  The weights e^(s_ij - m) of each key tile
+ * are rounded to E4M3 (after a fixed power-of-two shift, relative error at
+ * most 2^-4 for weights above 2^-13 of the running maximum) for the P.V
+ * product; the normaliser and lse use the fp32 weights.  O is therefore
+ * exact attention of the dequantised inputs up to that rounding of P.
+ * o: bf16 [B,H,Nq,d].  lse: fp32 [B,H,Nq] or NULL.  causal and window as
+ * fa_fwd.  No soft-cap.  d in {64, 128}.
+ * Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for a descale that is not
+ * finite and > 0 or a score factor scale*q_descale*k_descale beyond fp32
+ * range, FA_ERR_UNSUPPORTED for d not in {64, 128}.
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+               int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+               float scale, float q_descale, float k_descale, float v_descale,
+               int causal, int window, fa_stream_t stream);
+
+/*
  * fa_fwd_splitkv -- split-KV attention, first pass (bf16 q, k, v).
  *
  * The keys are cut into num_splits chunks of C = ceil(Nk / num_splits) keys;

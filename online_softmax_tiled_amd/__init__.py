@@ -8,11 +8,13 @@ from .fa import (  # noqa: F401
     FaError,
     RollingKVCache,
     attention,
+    attention_fp8,
     fa_combine,
     fa_decode_rolling,
     fa_fwd,
     fa_fwd_ex,
     fa_fwd_f32,
+    fa_fwd_fp8,
     fa_fwd_splitkv,
     fa_kv_append,
     fa_softmax,

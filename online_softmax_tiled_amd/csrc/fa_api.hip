@@ -148,6 +148,29 @@ int fa_fwd_ex(const fa_fwd_args *args) {
     return run_fwd(*args);
 }
 
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H, int64_t Hkv,
+               int64_t Nq, int64_t Nk, int64_t d, float scale, float q_descale, float k_descale, float v_descale,
+               int causal, int window, fa_stream_t stream) {
+    FwdParams p;
+    const int rc = validate_fwd(
+        make_args(FA_DTYPE_BF16, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, 0.0f, stream), p);
+    if (rc != FA_OK) return rc;
+    for (float f : {q_descale, k_descale, v_descale})
+        if (!isfinite(f) || !(f > 0.0f)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    // Scores in base-2 units: dot(q8, k8) * scale * q_descale * k_descale *
+    // log2(e).  A negative factor is applied as a sign flip of Q (exact in
+    // fp8), a zero one as the smallest normal float: every |dot| <= 448^2 *
+    // 128, so every weight is then exactly 1 (all visible keys equal).
+    double c = (double)scale * q_descale * k_descale * 1.4426950408889634;
+    if (!isfinite(c) || fabs(c) > 3.0e38) return FA_ERR_INVALID_ARG;
+    const uint32_t qflip = c < 0.0 ? 0x80808080u : 0u;
+    float c_log2 = (float)fabs(c);
+    if (c_log2 < 1.17549435e-38f) c_log2 = 1.17549435e-38f;
+    if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+    return fa::launch_fwd_fp8(p, (int)d, c_log2, v_descale, qflip, reinterpret_cast<hipStream_t>(stream));
+}
+
 int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o_part, float *m_part, float *l_part,
                    int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
                    int window, float softcap, int num_splits, fa_stream_t stream) {

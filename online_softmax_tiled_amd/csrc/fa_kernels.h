@@ -9,6 +9,10 @@ namespace fa {
 
 // bf16 tiled forward (MFMA).  split: write per-split partials instead of O.
 int launch_fwd_bf16(const FwdParams &p, int d, bool split, hipStream_t stream);
+// fp8 (E4M3) tiled forward (MFMA), bf16 output.  c_log2 > 0 multiplies the
+// integer-exact fp8 dot products into base-2 score units; out_scale
+// multiplies O; qflip is xor-ed into every 4 bytes of Q (0x80808080 negates Q).
+int launch_fwd_fp8(const FwdParams &p, int d, float c_log2, float out_scale, uint32_t qflip, hipStream_t stream);
 // fp32 tiled forward (VALU, fp32 throughout).
 int launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream);
 // bf16 split-KV partial pass for few query rows per K/V head (decode).

@@ -26,7 +26,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MAX_HEAD_WINDOWS = 256
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
             "fa_decode_rolling", "fa_softmax", "fa_softmax_topk", "fa_status_string")
 FA_MAX_TOPK = 64
 
@@ -77,6 +77,8 @@ def load_library():
     lib.fa_fwd.argtypes = fwd_args
     lib.fa_fwd_f32.argtypes = fwd_args
     lib.fa_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, f32, f32,
+                               ci, ci, vp]
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                    f32, ci, ci, f32, ci, vp]
     lib.fa_combine.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ci, ci, vp]
@@ -85,7 +87,7 @@ def load_library():
                                       f32, f32, ci, vp]
     lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, ci, vp]
     lib.fa_softmax_topk.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, vp]
-    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
+    for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
                  "fa_decode_rolling", "fa_softmax", "fa_softmax_topk"):
         getattr(lib, name).restype = ci
     lib.fa_status_string.argtypes = [ci]
@@ -183,6 +185,13 @@ def fa_softmax_topk(x, probs, indices, lse, rows, n, k, dtype, stream=None):
                                            int(dtype), _stream(stream)),
            "fa_softmax_topk")
 
+def fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale, causal, window,
+               stream=None):
+    _check(load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                                     float(scale), float(q_descale), float(k_descale), float(v_descale),
+                                     int(causal), int(window), _stream(stream)),
+           "fa_fwd_fp8")
+
 
 # ------------------------------------------------------------- conveniences
 def _shapes(q, k, v):
@@ -222,6 +231,22 @@ def attention(q, k, v, scale=None, causal=False, window=0, head_window=None, sof
         fa_fwd(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap)
     else:
         fa_fwd_f32(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap)
+    return o, lse
+
+
+def attention_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, scale=None, causal=False, window=0,
+                  out=None, lse=None):
+    """fp8 attention: q [B,H,Nq,d], k, v [B,Hkv,Nk,d] hold OCP E4M3 bytes
+    (torch.float8_e4m3fn or torch.uint8) whose values are multiplied by the
+    descale factors.  Returns (o bf16 [B,H,Nq,d], lse fp32 [B,H,Nq])."""
+    import torch
+    if q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise ValueError("q, k, v must be float8_e4m3fn or uint8 (E4M3 bytes)")
+    B, H, Hkv, Nq, Nk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale, causal, window)
     return o, lse
 
 

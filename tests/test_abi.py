@@ -177,3 +177,33 @@ def test_softmax_validation():
     assert lib.fa_softmax_topk(*t, 4, 7, FAKE) == fa.FA_ERR_INVALID_ARG        # unknown dtype
     t4 = list(t); t4[5] = 1 << 31
     assert lib.fa_softmax_topk(*t4, 4, B, FAKE) == fa.FA_ERR_UNSUPPORTED
+
+
+def call_fp8(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, H=4, Hkv=2, Nq=8, Nk=8, d=128, scale=0.125,
+             qd=1.0, kd=1.0, vd=1.0, causal=0, window=0, stream=FAKE)
+    a.update(over)
+    return fa.load_library().fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                                        a["Nq"], a["Nk"], a["d"], a["scale"], a["qd"], a["kd"], a["vd"],
+                                        a["causal"], a["window"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(qd=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(kd=-2.0), fa.FA_ERR_INVALID_ARG),
+    (dict(vd=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(vd=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=3e38, qd=3e38), fa.FA_ERR_INVALID_ARG),   # score factor beyond fp32
+    (dict(H=3), fa.FA_ERR_INVALID_ARG),
+    (dict(window=4), fa.FA_ERR_INVALID_ARG),
+    (dict(v=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),                  # fp8 kernels: d in {64, 128}
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fp8_validation(over, status):
+    assert call_fp8(**over) == status
+
+
+def test_fp8_empty_is_a_no_op():
+    assert call_fp8(Nq=0, q=None, o=None) == fa.FA_OK
