@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|prefill_fp8]
                     [--no-cpu-baseline] [--no-decode]
     python bench.py --summarize-profiles DIR   (host only: rocprofv3 CSVs -> profiles/)
 
@@ -17,7 +17,10 @@ A step is one forward pass over one batch of synthetic input:
   + ``fa_combine`` (B=16, H=32, Hkv=8, d=128, window 4096, 4 sinks, 4
   splits, position 65535), in GB/s;
 * softmax (same condition): ``fa_softmax`` (online normaliser) and
-  ``fa_softmax_topk`` (k = 8) on 512 rows of 256000 fp32 logits, in GB/s.
+  ``fa_softmax_topk`` (k = 8) on 512 rows of 256000 fp32 logits, in GB/s;
+* prefill_fp8 (same condition; ``--workload prefill_fp8`` runs it alone):
+  ``fa_fwd_fp8`` on the causal prefill shape with E4M3 Q, K, V, in TFLOP/s
+  against the 5 PFLOP/s dense fp8 peak.
 
 Inputs are seeded synthetic tensors (online_softmax_tiled_amd.workloads),
 resident in HBM before timing starts.  Kernel durations are taken with HIP
@@ -42,14 +45,18 @@ sys.path.insert(0, ROOT)
 from online_softmax_tiled_amd import workloads as wl  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)"
 PREFILL = "bf16_causal_b4_h32_n4096_d128"
 DECODE = "bf16_splitkv_decode_b16_h32kv8_nk32768_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
-    "prefill": ["online_softmax_tiled_amd/csrc/fa_fwd_bf16.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
+    "prefill": ["online_softmax_tiled_amd/csrc/fa_fwd_bf16.hip", "online_softmax_tiled_amd/csrc/fa_tile.h",
+                "online_softmax_tiled_amd/csrc/fa_device.h"],
     "decode": ["online_softmax_tiled_amd/csrc/fa_splitkv.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
+    "prefill_fp8": ["online_softmax_tiled_amd/csrc/fa_fwd_fp8.hip", "online_softmax_tiled_amd/csrc/fa_tile.h",
+                    "online_softmax_tiled_amd/csrc/fa_device.h"],
 }
 
 
@@ -117,6 +124,30 @@ def bench_prefill(torch, fa, steps, warmup):
         "value": flops * steps / (total * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+
+
+def bench_prefill_fp8(torch, fa, steps, warmup):
+    w = wl.FP8_PREFILL
+    x = wl.generate_fp8(w)
+    t = {n: torch.from_numpy(x[n]).cuda() for n in "qkv"}
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    args = (t["q"], t["k"], t["v"], o, lse, w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.scale, x["q_descale"],
+            x["k_descale"], x["v_descale"], int(w.causal), w.window)
+
+    def launch():
+        fa.fa_fwd_fp8(*args)
+
+    avg, total, wall = time_launches(launch, steps, warmup, torch)
+    flops = wl.algorithmic_flops(w)
+    achieved = flops / (avg * 1e-3) / 1e12
+    return w, {
+        "flops": flops, "avg_ms": avg, "total_ms": total, "wall_s": wall,
+        "value": flops * steps / (total * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill_fp8")},
     }
 
 
@@ -236,8 +267,13 @@ def bench_softmax(torch, fa, steps, warmup):
 def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
     """Time the fp64 oracle on a strided row sample of workload ``w``."""
     import oracle
-    inp = wl.generate(w)
-    q, k, v = (inp[n].astype(np.float64) for n in "qkv")
+    if w.dtype == "fp8":
+        from oracle import fp8 as ofp8
+        x = wl.generate_fp8(w)
+        q, k, v = (ofp8.dequantise(x[n], x[n + "_descale"]) for n in "qkv")
+    else:
+        inp = wl.generate(w)
+        q, k, v = (inp[n].astype(np.float64) for n in "qkv")
     total = w.B * w.H * w.Nq
     threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
     hw = list(w.head_window) if w.head_window else None
@@ -281,13 +317,19 @@ PROFILE_RUNS = {
                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload decode",
     "WRITE_SIZE_decode": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_decode -o run -- "
                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload decode",
+    "trace_prefill_fp8": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_prefill_fp8 -o run -- "
+                         "python bench.py --no-cpu-baseline --workload prefill_fp8",
+    "FETCH_SIZE_prefill_fp8": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE_prefill_fp8 -o run "
+                              "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload prefill_fp8",
+    "WRITE_SIZE_prefill_fp8": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_prefill_fp8 -o run "
+                              "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload prefill_fp8",
     "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_FETCH_SIZE -o run -- "
                        "python bench.py --copy-calibration",
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
                        "python bench.py --copy-calibration",
 }
 KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
-           "combine": "combine_kernel<128>", "copy": "__amd_rocclr_copyBuffer"}
+           "combine": "combine_kernel<128>", "prefill_fp8": "fwd_fp8_kernel<128>", "copy": "__amd_rocclr_copyBuffer"}
 
 
 def _csv(path):
@@ -315,7 +357,7 @@ def summarize_profiles(d):
     """Write profiles/hbm_traffic.json and the two kernel-trace summaries
     from the rocprofv3 output under d (the runs in PROFILE_RUNS)."""
     cmds = {k: v.format(d=d) for k, v in PROFILE_RUNS.items()}
-    leg = {"prefill": "prefill", "decode": "decode", "combine": "decode"}
+    leg = {"prefill": "prefill", "decode": "decode", "combine": "decode", "prefill_fp8": "prefill_fp8"}
 
     def stat(kernel, run):
         stats = {r["Name"]: r for r in _csv(os.path.join(d, run, "*kernel_stats.csv"))}
@@ -335,11 +377,12 @@ def summarize_profiles(d):
                 "(__amd_rocclr_copyBuffer).  bench.py reports these only while source_hash matches the "
                 "kernel sources.  Written by: python bench.py --summarize-profiles DIR.",
         "commands": [cmds[k] for k in ("FETCH_SIZE_prefill", "WRITE_SIZE_prefill", "FETCH_SIZE_decode",
-                                       "WRITE_SIZE_decode", "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
+                                       "WRITE_SIZE_decode", "FETCH_SIZE_prefill_fp8", "WRITE_SIZE_prefill_fp8",
+                                       "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1)},
     }
     hbm = {}
-    for kind in ("prefill", "decode", "combine"):
+    for kind in ("prefill", "decode", "combine", "prefill_fp8"):
         f = _counter_kib(d, "FETCH_SIZE_" + leg[kind], KERNELS[kind])
         w_ = _counter_kib(d, "WRITE_SIZE_" + leg[kind], KERNELS[kind])
         rb, wb = f * 1024 * fs, w_ * 1024 * ws
@@ -419,7 +462,34 @@ hbm_traffic.json): split kernel read {rb / 1e9:.3f} GB, written {wb / 1e6:.2f} M
 """
     with open(os.path.join(ROOT, "profiles", f"splitkv_decode_b16_h32kv8_nk32768_d128.md"), "w") as f:
         f.write(md)
-    print(json.dumps({k: traffic[k]["bytes_per_launch"] for k in ("prefill", "decode", "combine")}))
+    w8 = wl.FP8_PREFILL
+    name, calls, avg, mn, mx = stat(KERNELS["prefill_fp8"], "trace_prefill_fp8")
+    flops = wl.algorithmic_flops(w8)
+    rb, wb = hbm["prefill_fp8"]
+    md = f"""# fwd_fp8_kernel on the causal prefill shape with E4M3 inputs (B=4, H=32, Nq=Nk=4096, d=128)
+
+Command (run from the repository root on one MI355X):
+
+    {cmds["trace_prefill_fp8"]}
+
+Kernel trace statistics (`run_kernel_stats.csv`; every dispatch of the run,
+warm-up included):
+
+| kernel | calls | average (us) | min (us) | max (us) |
+|---|---|---|---|---|
+| {name[:90]} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} |
+
+Algorithmic work per launch: {flops:,} FLOP.  At the trace's average duration
+this is {flops / (avg * 1e-6) / 1e12:.0f} TFLOP/s ({flops / (avg * 1e-6) / 1e12 / PEAK_FP8_TFLOPS * 100:.1f}% of the 5 PFLOP/s dense fp8 peak,
+{flops / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS * 100:.1f}% of the bf16 one).
+
+HBM traffic per launch (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy):
+read {rb / 1e6:.1f} MB, written {wb / 1e6:.1f} MB, against {wl.algorithmic_bytes(w8) / 1e6:.1f} MB of algorithmic
+bytes (one-byte Q, K, V read once, bf16 O and fp32 lse written once).
+"""
+    with open(os.path.join(ROOT, "profiles", "fwd_fp8_causal_b4_h32_n4096_d128.md"), "w") as f:
+        f.write(md)
+    print(json.dumps({k: traffic[k]["bytes_per_launch"] for k in ("prefill", "decode", "combine", "prefill_fp8")}))
 
 
 def main():
@@ -427,7 +497,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", choices=["prefill", "decode"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "decode", "prefill_fp8"], default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="prefill leg only (no decode or rolling legs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -457,7 +527,7 @@ def main():
     torch.cuda.init()
 
     main_w, leg = None, None
-    decode = rolling = softmax = None
+    decode = rolling = softmax = fp8 = None
     if args.workload == "prefill":
         main_w, leg = bench_prefill(torch, fa, args.steps, args.warmup)
         print(f"[bench] prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
@@ -470,7 +540,13 @@ def main():
             softmax = bench_softmax(torch, fa, args.steps, args.warmup)
             print(f"[bench] softmax done: {softmax['softmax']['ms_per_step']:.4f} ms, top-k "
                   f"{softmax['topk']['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
+            _, fp8 = bench_prefill_fp8(torch, fa, args.steps, args.warmup)
+            print(f"[bench] fp8 prefill done: {fp8['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
         value, unit = leg["value"], "TFLOP/s"
+    elif args.workload == "prefill_fp8":
+        main_w, leg = bench_prefill_fp8(torch, fa, args.steps, args.warmup)
+        value, unit = leg["value"], "TFLOP/s"
+        print(f"[bench] fp8 prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
     else:
         main_w, leg = bench_decode(torch, fa, args.steps, args.warmup)
         value, unit = leg["value"], "GB/s"
@@ -480,7 +556,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(leg["total_ms"] / args.steps, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if args.workload == "prefill_fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "num_splits": w.num_splits or None, "parallelism": "none (1 GPU)"},
@@ -495,6 +572,11 @@ def main():
         out["rolling"] = rolling
     if softmax is not None:
         out["softmax"] = softmax
+    if fp8 is not None:
+        w8 = wl.FP8_PREFILL
+        out["prefill_fp8"] = {"workload": w8.name, "value": round(fp8["value"], 2), "unit": "TFLOP/s",
+                              "ms_per_step": round(fp8["total_ms"] / args.steps, 4), "dtype": "fp8 e4m3 (bf16 out)",
+                              "roofline": fp8["roofline"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)

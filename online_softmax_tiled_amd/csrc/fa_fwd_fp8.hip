@@ -35,7 +35,12 @@
 //     so that its transposing reads are conflict-free, and turns every 4x4
 //     byte block (4 keys x 4 columns) into 4 V^T dwords with 8 v_perm_b32;
 //   * the lazy-rescale threshold is small (TAU = 1.5): weights stay below
-//     2^(TAU + P_SHIFT) = 2^8.5, inside e4m3's range (largest value 448).
+//     2^(TAU + P_SHIFT) = 2^8.5, inside e4m3's range (largest value 448);
+//   * with half the matrix work of bf16 per tile, the vector phase (its
+//     exps issue at a quarter of the VALU rate) is the longer one, so it
+//     holds only the mask, the maximum and the exps: the fp32 weights are
+//     summed and rounded to E4M3 in the next matrix phase, while the P.V
+//     MFMAs run.
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_tile.h"
@@ -43,6 +48,12 @@
 namespace fa {
 
 namespace {
+
+// Selects the masked or the unmasked softmax of a step at compile time.
+template <bool B>
+struct MaskTag {
+    static constexpr bool value = B;
+};
 
 constexpr int NW = 8;        // waves per workgroup (two per SIMD)
 constexpr int BM = NW * 32;  // query rows per workgroup
@@ -137,7 +148,7 @@ struct Wave8 {
     // the factor), fp32 weights 2^(t - m + P_SHIFT) summed into l and
     // rounded to e4m3 as the P^T operand.
     template <bool MASK>
-    __device__ __forceinline__ bool softmax(f32x16 (&sacc)[2], int it, i32x8 &pf, float &alpha) {
+    __device__ __forceinline__ bool softmax(f32x16 (&sacc)[2], int it, f32x16 (&pw)[2], float &alpha) {
         if (MASK) {
             // Key ko = c + 4*hf of the tile is visible iff lo <= ko < hi.
             const int lo = lo_rel - it * BN, hi = hi_rel - it * BN;
@@ -167,21 +178,9 @@ struct Wave8 {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) sacc[kb][j] = fast_exp2(fmaf(sacc[kb][j], c_log2, bias));
-        float rs[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            rs[i] = (sacc[i / 4][4 * (i % 4)] + sacc[i / 4][4 * (i % 4) + 1]) +
-                    (sacc[i / 4][4 * (i % 4) + 2] + sacc[i / 4][4 * (i % 4) + 3]);
-        l = l * alpha + (((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7])));
-        // Byte e of the operand is element e % 16 of half e / 16.
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][4 * q], sacc[kb][4 * q + 1], 0, false);
-                pf[4 * kb + q] = __builtin_amdgcn_cvt_pk_fp8_f32(sacc[kb][4 * q + 2], sacc[kb][4 * q + 3], lo2, true);
-            }
+            for (int j = 0; j < 16; ++j) pw[kb][j] = fast_exp2(fmaf(sacc[kb][j], c_log2, bias));
+        // Their sum and E4M3 rounding are left to the next matrix phase (pv).
+        l *= alpha;
         return move;
     }
 
@@ -192,9 +191,26 @@ struct Wave8 {
             for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
     }
 
-    // O^T += V^T P^T: row db*32 + lane%32 of V^T, permuted keys 32*hf + [0, 32).
-    __device__ __forceinline__ void pv(const uint8_t *vt, const i32x8 &pf) {
+    // O^T += V^T P^T: row db*32 + lane%32 of V^T, permuted keys 32*hf + [0,
+    // 32).  The weights pw (fp32) are rounded to E4M3 here (byte e of the
+    // operand is element e % 16 of half e / 16), and their fp32 sum is added
+    // to l while the MFMAs run.
+    __device__ __forceinline__ void pv(const uint8_t *vt, const f32x16 (&pw)[2]) {
         const char *Vb = reinterpret_cast<const char *>(vt);
+        i32x8 pf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(pw[kb][4 * q], pw[kb][4 * q + 1], 0, false);
+                pf[4 * kb + q] = __builtin_amdgcn_cvt_pk_fp8_f32(pw[kb][4 * q + 2], pw[kb][4 * q + 3], lo2, true);
+            }
+        float rs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rs[i] = (pw[i / 4][4 * (i % 4)] + pw[i / 4][4 * (i % 4) + 1]) +
+                    (pw[i / 4][4 * (i % 4) + 2] + pw[i / 4][4 * (i % 4) + 3]);
+        l += ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7]));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const u32x4 a0 = *reinterpret_cast<const u32x4 *>(Vb + db * 32 * L::VT_ROW + vko[0]);
@@ -336,10 +352,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(const FwdParams p, const
         for (int u = 0; u < L::LPW; ++u)
             buffer_load_lds16(V, head_bytes, (lds_void *)(vstage + (lw * L::LPW + u) * 1024), v_goff[u], toff);
     };
-    auto is_full = [&](int t) {
-        const int64_t kt = kbeg + (int64_t)t * BN;
-        return kt >= full_lo && kt + BN <= full_hi;
-    };
     // This loading wave's region of the staged V tile -> V^T tile vt (only
     // its own loads are read, so its own wait suffices).
     auto transpose_v = [&](uint8_t *vt) {
@@ -362,23 +374,25 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(const FwdParams p, const
     };
 
     f32x16 sacc[2];
-    i32x8 pf;
+    f32x16 pw[2];  // fp32 weights of the tile whose P.V is next
     // Step j: matrix phase (loads of K_{j+1} and V_j by the leaders, scores
-    // of tile j, P.V of tile j-1), barrier, vector phase (softmax of tile j;
-    // the leaders then wait for their loads and transpose their part of V_j),
-    // barrier.  Waves 4..7 run one phase behind waves 0..3.
-    auto step = [&](int j, const uint8_t *kcur, const uint8_t *vtprev, uint8_t *knext, uint8_t *vtcur) {
+    // of tile j, P.V of tile j-1 with the sum and rounding of its weights),
+    // barrier, vector phase (mask, maximum and exps of tile j; the leaders
+    // then wait for their loads and transpose their part of V_j), barrier.
+    // Waves 4..7 run one phase behind waves 0..3.
+    auto step = [&](auto mask, int j, const uint8_t *kcur, const uint8_t *vtprev, uint8_t *knext,
+                    uint8_t *vtcur) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask)::value;
         if (leader) {
             if (j + 1 < ntiles) load_k(j + 1, knext);
             if (j < ntiles) load_v(j);
         }
         if (j < ntiles) st.scores(kcur, sacc);
-        if (j >= 1) st.pv(vtprev, pf);
+        if (j >= 1) st.pv(vtprev, pw);
         lds_barrier();
         if (j < ntiles) {
             float alpha;
-            const bool move = is_full(j) ? st.template softmax<false>(sacc, j, pf, alpha)
-                                         : st.template softmax<true>(sacc, j, pf, alpha);
+            const bool move = st.template softmax<MASK>(sacc, j, pw, alpha);
             if (move) st.rescale(alpha);
         }
         if (leader) {
@@ -392,11 +406,32 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(const FwdParams p, const
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     if (!leader) lds_barrier();
-    for (int j = 0; j <= ntiles; j += 2) {
-        step(j, kbuf0, vt1, kbuf1, vt0);
-        if (j + 1 > ntiles) break;
-        step(j + 1, kbuf1, vt0, kbuf0, vt1);
-    }
+    // Tiles [t_a, t_b) are seen in full by every row of the block (tile t
+    // starts at key kbeg + 64 t); the others need the mask.  One loop per
+    // kind keeps the masked/unmasked choice out of the loop body: a branch
+    // there makes the two softmax variants merge their registers, which
+    // costs about 50 VGPRs and copies.
+    const int t_a = min(ntiles, (int)((full_lo - kbeg + BN - 1) / BN));
+    const int t_b = max(t_a, min(ntiles, (int)((full_hi - kbeg) / BN)));
+    // Steps j0 .. j1-1; tile j's K sits in kbuf[j % 2], its V^T in vt[j % 2].
+    auto run = [&](auto mask, int j0, int j1) __attribute__((always_inline)) {
+        int j = j0;
+        if (j < j1 && (j & 1)) {
+            step(mask, j, kbuf1, vt0, kbuf0, vt1);
+            ++j;
+        }
+        for (; j + 1 < j1; j += 2) {
+            step(mask, j, kbuf0, vt1, kbuf1, vt0);
+            step(mask, j + 1, kbuf1, vt0, kbuf0, vt1);
+        }
+        if (j < j1) step(mask, j, kbuf0, vt1, kbuf1, vt0);
+    };
+    run(MaskTag<true>(), 0, t_a);
+    run(MaskTag<false>(), t_a, t_b);
+    run(MaskTag<true>(), t_b, ntiles);
+    // last step: P.V of the last tile only
+    if (ntiles & 1) step(MaskTag<false>(), ntiles, kbuf1, vt0, kbuf0, vt1);
+    else step(MaskTag<false>(), ntiles, kbuf0, vt1, kbuf1, vt0);
     if (leader) lds_barrier();
 
     // ---- epilogue: O = v_descale * acc / l.  Lane holds dims db*32 +
