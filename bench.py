@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|prefill_fp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|prefill_fp8|rolling|softmax]
                     [--no-cpu-baseline] [--no-decode]
     python bench.py --summarize-profiles DIR   (host only: rocprofv3 CSVs -> profiles/)
 
@@ -18,6 +18,9 @@ A step is one forward pass over one batch of synthetic input:
   splits, position 65535), in GB/s;
 * softmax (same condition): ``fa_softmax`` (online normaliser) and
   ``fa_softmax_topk`` (k = 8) on 512 rows of 256000 fp32 logits, in GB/s;
+``--workload rolling`` and ``--workload softmax`` run only that leg and print
+its object (for profiling those kernels in runs of their own).
+
 * prefill_fp8 (same condition; ``--workload prefill_fp8`` runs it alone):
   ``fa_fwd_fp8`` on the causal prefill shape with E4M3 Q, K, V, in TFLOP/s
   against the 5 PFLOP/s dense fp8 peak.
@@ -57,6 +60,9 @@ KERNEL_SOURCES = {
     "decode": ["online_softmax_tiled_amd/csrc/fa_splitkv.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
     "prefill_fp8": ["online_softmax_tiled_amd/csrc/fa_fwd_fp8.hip", "online_softmax_tiled_amd/csrc/fa_tile.h",
                     "online_softmax_tiled_amd/csrc/fa_device.h"],
+    "rolling_decode": ["online_softmax_tiled_amd/csrc/fa_splitkv.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
+    "softmax": ["online_softmax_tiled_amd/csrc/fa_softmax.hip"],
+    "topk": ["online_softmax_tiled_amd/csrc/fa_softmax.hip"],
 }
 
 
@@ -231,7 +237,7 @@ def bench_rolling(torch, fa, steps, warmup):
         "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "d": w.d, "window": w.window, "sinks": w.sinks,
                    "pos": w.pos, "cache_rows_read": w.rows, "num_splits": S},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("rolling_decode"),
                      "kernel": "splitkv_decode_kernel (rolling cache)", "avg_ms": round(avg_dec, 4)},
     }
 
@@ -258,7 +264,7 @@ def bench_softmax(torch, fa, steps, warmup):
         avg, total, _ = time_launches(fn, steps, warmup, torch)
         gbs = nbytes / (avg * 1e-3) / 1e9
         out[name] = {"ms_per_step": round(avg, 4), "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
-                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name)}
     out["softmax"]["bytes_note"] = "two reads of x and one write of y (online normaliser)"
     out["topk"]["bytes_note"] = "one read of x; k probabilities and indices written"
     return out
@@ -323,13 +329,28 @@ PROFILE_RUNS = {
                               "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload prefill_fp8",
     "WRITE_SIZE_prefill_fp8": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_prefill_fp8 -o run "
                               "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload prefill_fp8",
+    "trace_rolling": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_rolling -o run -- "
+                     "python bench.py --no-cpu-baseline --workload rolling",
+    "trace_softmax": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace_softmax -o run -- "
+                     "python bench.py --no-cpu-baseline --workload softmax",
+    "FETCH_SIZE_rolling": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE_rolling -o run -- "
+                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload rolling",
+    "WRITE_SIZE_rolling": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_rolling -o run -- "
+                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload rolling",
+    "FETCH_SIZE_softmax": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/FETCH_SIZE_softmax -o run -- "
+                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload softmax",
+    "WRITE_SIZE_softmax": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/WRITE_SIZE_softmax -o run -- "
+                          "python bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload softmax",
     "copy_FETCH_SIZE": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_FETCH_SIZE -o run -- "
                        "python bench.py --copy-calibration",
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
                        "python bench.py --copy-calibration",
 }
 KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
-           "combine": "combine_kernel<128>", "prefill_fp8": "fwd_fp8_kernel<128>", "copy": "__amd_rocclr_copyBuffer"}
+           "combine": "combine_kernel<128>", "prefill_fp8": "fwd_fp8_kernel<128>",
+           "rolling_decode": "splitkv_decode_kernel<128, 4, false>", "kv_append": "kv_append_kernel<128>",
+           "softmax": "softmax_kernel<false, 4>", "topk": "softmax_topk_kernel<false, 4>",
+           "copy": "__amd_rocclr_copyBuffer"}
 
 
 def _csv(path):
@@ -357,7 +378,8 @@ def summarize_profiles(d):
     """Write profiles/hbm_traffic.json and the two kernel-trace summaries
     from the rocprofv3 output under d (the runs in PROFILE_RUNS)."""
     cmds = {k: v.format(d=d) for k, v in PROFILE_RUNS.items()}
-    leg = {"prefill": "prefill", "decode": "decode", "combine": "decode", "prefill_fp8": "prefill_fp8"}
+    leg = {"prefill": "prefill", "decode": "decode", "combine": "decode", "prefill_fp8": "prefill_fp8",
+           "rolling_decode": "rolling", "softmax": "softmax", "topk": "softmax"}
 
     def stat(kernel, run):
         stats = {r["Name"]: r for r in _csv(os.path.join(d, run, "*kernel_stats.csv"))}
@@ -378,11 +400,12 @@ def summarize_profiles(d):
                 "kernel sources.  Written by: python bench.py --summarize-profiles DIR.",
         "commands": [cmds[k] for k in ("FETCH_SIZE_prefill", "WRITE_SIZE_prefill", "FETCH_SIZE_decode",
                                        "WRITE_SIZE_decode", "FETCH_SIZE_prefill_fp8", "WRITE_SIZE_prefill_fp8",
-                                       "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
+                                       "FETCH_SIZE_rolling", "WRITE_SIZE_rolling", "FETCH_SIZE_softmax",
+                                       "WRITE_SIZE_softmax", "copy_FETCH_SIZE", "copy_WRITE_SIZE")],
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1)},
     }
     hbm = {}
-    for kind in ("prefill", "decode", "combine", "prefill_fp8"):
+    for kind in ("prefill", "decode", "combine", "prefill_fp8", "rolling_decode", "softmax", "topk"):
         f = _counter_kib(d, "FETCH_SIZE_" + leg[kind], KERNELS[kind])
         w_ = _counter_kib(d, "WRITE_SIZE_" + leg[kind], KERNELS[kind])
         rb, wb = f * 1024 * fs, w_ * 1024 * ws
@@ -489,7 +512,73 @@ bytes (one-byte Q, K, V read once, bf16 O and fp32 lse written once).
 """
     with open(os.path.join(ROOT, "profiles", "fwd_fp8_causal_b4_h32_n4096_d128.md"), "w") as f:
         f.write(md)
-    print(json.dumps({k: traffic[k]["bytes_per_launch"] for k in ("prefill", "decode", "combine", "prefill_fp8")}))
+    wr = wl.ROLLING
+    rows = []
+    for kind in ("kv_append", "rolling_decode", "combine"):
+        rows.append(stat(KERNELS[kind], "trace_rolling"))
+    dec_bytes = (2 * wr.rows * wr.B * wr.Hkv * wr.d * 2 + wr.B * wr.H * wr.d * 2
+                 + wr.B * wr.H * wr.num_splits * (wr.d + 2) * 4)
+    davg = rows[1][2]
+    rb, wb = hbm["rolling_decode"]
+    table = "\n".join(f"| {n[:90]} | {c} | {a:.1f} | {mn_:.1f} | {mx_:.1f} |" for n, c, a, mn_, mx_ in rows)
+    md = f"""# Streaming decode over a rolling KV cache with attention sinks (B=16, H=32, Hkv=8, d=128, window 4096, 4 sinks, position 65535, 4 splits, bf16)
+
+Command (run from the repository root on one MI355X):
+
+    {cmds["trace_rolling"]}
+
+Kernel trace statistics (`run_kernel_stats.csv`; one step = append + decode
++ combine, and the decode kernel also alone; warm-up included):
+
+| kernel | calls | average (us) | min (us) | max (us) |
+|---|---|---|---|---|
+{table}
+
+Decode kernel: {dec_bytes:,} algorithmic bytes per launch (the {wr.rows} filled
+cache rows of K and V per (batch, K/V head) read once, Q read, fp32 partials
+written); at the trace's average duration {dec_bytes / (davg * 1e-6) / 1e9:.0f} GB/s
+({dec_bytes / (davg * 1e-6) / 1e9 / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s).  HBM traffic per decode launch (FETCH_SIZE /
+WRITE_SIZE scaled by a 1 GiB copy): read {rb / 1e6:.1f} MB, written {wb / 1e6:.1f} MB.
+"""
+    with open(os.path.join(ROOT, "profiles", "rolling_decode_b16_h32kv8_w4096_s4_d128.md"), "w") as f:
+        f.write(md)
+
+    ws_ = wl.SOFTMAX
+    sb = wl.softmax_bytes(ws_)
+    lines = []
+    for kind, nb, what in (("softmax", sb["softmax_online"], "two reads of x, one write of y"),
+                           ("topk", sb["topk_fused"], "one read of x, k pairs written")):
+        name, calls, avg, mn, mx = stat(KERNELS[kind], "trace_softmax")
+        rb, wb = hbm[kind]
+        lines.append((name, calls, avg, mn, mx, nb, what, rb, wb))
+    table = "\n".join(f"| {n[:60]} | {c} | {a:.1f} | {mn_:.1f} | {mx_:.1f} |" for n, c, a, mn_, mx_, *_ in lines)
+    detail = "\n".join(
+        f"* {n.split('(')[0]}: {nb:,} algorithmic bytes ({what}); {nb / (a * 1e-6) / 1e9:.0f} GB/s at the "
+        f"average duration ({nb / (a * 1e-6) / 1e9 / PEAK_HBM_GBS * 100:.1f}% of 8 TB/s); HBM read "
+        f"{rb / 1e6:.1f} MB, written {wb / 1e6:.1f} MB (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy)."
+        for n, c, a, mn_, mx_, nb, what, rb, wb in lines)
+    md = f"""# Row softmax (online normaliser) and fused softmax top-k on 512 rows of 256000 fp32 logits (k = 8)
+
+Command (run from the repository root on one MI355X):
+
+    {cmds["trace_softmax"]}
+
+Kernel trace statistics (`run_kernel_stats.csv`; warm-up included):
+
+| kernel | calls | average (us) | min (us) | max (us) |
+|---|---|---|---|---|
+{table}
+
+{detail}
+
+A row (1 MB) is larger than on-chip memory and x (524 MB) larger than the
+256 MB Infinity Cache, so the softmax's second read comes from HBM again:
+its HBM read bytes are twice x.
+"""
+    with open(os.path.join(ROOT, "profiles", "softmax_fp32_rows512_n256000.md"), "w") as f:
+        f.write(md)
+    print(json.dumps({k: traffic[k]["bytes_per_launch"] for k in ("prefill", "decode", "combine", "prefill_fp8",
+                                                                  "rolling_decode", "softmax", "topk")}))
 
 
 def main():
@@ -497,7 +586,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", choices=["prefill", "decode", "prefill_fp8"], default="prefill")
+    ap.add_argument("--workload", choices=["prefill", "decode", "prefill_fp8", "rolling", "softmax"],
+                    default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="prefill leg only (no decode or rolling legs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -526,6 +616,10 @@ def main():
     fa.load_library()
     torch.cuda.init()
 
+    if args.workload in ("rolling", "softmax"):
+        r = (bench_rolling if args.workload == "rolling" else bench_softmax)(torch, fa, args.steps, args.warmup)
+        print(json.dumps({"leg": args.workload, **r}), flush=True)
+        return
     main_w, leg = None, None
     decode = rolling = softmax = fp8 = None
     if args.workload == "prefill":
