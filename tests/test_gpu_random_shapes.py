@@ -1,0 +1,72 @@
+"""Seeded random shapes for the forward kernels against the oracle: random
+batch, head group, query and key lengths (ragged against the 256-row query
+tiles and 64-key tiles), head size, causal / window / soft-cap choices.
+Tolerances are those of tests/test_gpu_parity.py (bf16, fp32) and
+tests/test_gpu_fp8.py (fp8 bounds from E4M3 rounding and the fp8
+instruction's accumulation)."""
+import math
+
+import numpy as np
+import pytest
+
+import test_gpu_fp8 as t8
+import test_gpu_parity as tp
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_softmax_tiled_amd as fa
+    fa.load_library()
+    yield
+
+
+def draw_shape(rng, ds):
+    Hkv = int(rng.choice([1, 2, 4]))
+    H = Hkv * int(rng.choice([1, 2, 3, 4]))
+    B = int(rng.integers(1, 3))
+    Nk = int(rng.integers(1, 700))
+    u = rng.random()
+    Nq = 1 if u < 0.2 else (int(rng.integers(1, 600)) if u < 0.6 else Nk)
+    d = int(rng.choice(ds))
+    causal = rng.random() < 0.6
+    window = int(rng.integers(1, 300)) if causal and rng.random() < 0.5 else 0
+    return B, H, Hkv, Nq, Nk, d, causal, window
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_bf16_random_shapes(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B, H, Hkv, Nq, Nk, d, causal, window = draw_shape(rng, [32, 64, 128])
+    softcap = float(rng.choice([0.0, 0.0, 20.0]))
+    what = f"bf16 seed={seed} B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} W={window} cap={softcap}"
+    print("case", what, flush=True)
+    inp = tp.rand_inputs(B, H, Hkv, Nq, Nk, d, seed=seed, dtype="bf16")
+    tp.parity(inp, "bf16", 1.0 / math.sqrt(d), causal=causal, window=window, softcap=softcap, what=what)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fp32_random_shapes(seed):
+    rng = np.random.default_rng(2000 + seed)
+    B, H, Hkv, Nq, Nk, d, causal, window = draw_shape(rng, [32, 64, 128])
+    what = f"fp32 seed={seed} B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} W={window}"
+    print("case", what, flush=True)
+    inp = tp.rand_inputs(B, H, Hkv, Nq, Nk, d, seed=seed, dtype="fp32", dist="uniform")
+    tp.parity(inp, "fp32", 1.0 / math.sqrt(d), causal=causal, window=window, what=what)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fp8_random_shapes(seed):
+    rng = np.random.default_rng(3000 + seed)
+    B, H, Hkv, Nq, Nk, d, causal, window = draw_shape(rng, [64, 128])
+    family = ("narrow", "full range")[seed % 2]
+    what = (f"fp8 {family} seed={seed} B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} "
+            f"W={window}")
+    print("case", what, flush=True)
+    make = t8.narrow_inputs if family == "narrow" else t8.random_inputs
+    t8.check(make(B, H, Hkv, Nq, Nk, d, seed=seed), 1.0 / math.sqrt(d), causal, window, what)
