@@ -354,6 +354,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
         key_bounds(qrow + off, Nk, p.causal, W, lo, hi);
         lo = (lo > r_lo ? lo : r_lo) - kbeg;
         hi = (hi < r_hi ? hi : r_hi) - kbeg;
+        // A row whose keys all lie outside this split has hi < lo here; an
+        // empty interval keeps the mask's unsigned span at 0 (not 2^32 - 1).
+        if (hi < lo) hi = lo;
         st.lo_rel[0] = (int)(lo < -1 ? -1 : (lo > 0x3fffffff ? 0x3fffffff : lo));
         st.hi_rel[0] = (int)(hi < -1 ? -1 : (hi > 0x3fffffff ? 0x3fffffff : hi));
 #pragma unroll

@@ -267,6 +267,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(const FwdParams p, const
         key_bounds(qrow + off, Nk, p.causal, W, lo, hi);
         lo -= kbeg;
         hi -= kbeg;
+        if (hi < lo) hi = lo;  // empty interval: the mask's unsigned span stays 0
         st.lo_rel = (int)(lo < -1 ? -1 : (lo > 0x3fffffff ? 0x3fffffff : lo));
         st.hi_rel = (int)(hi < -1 ? -1 : (hi > 0x3fffffff ? 0x3fffffff : hi));
         // Q^T operand of k-step ds: bytes 64*ds + 32*hf + [0, 32) of this row.

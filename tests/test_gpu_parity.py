@@ -276,7 +276,7 @@ def test_splitkv_decode_workload_full():
         assert np.allclose(lp.reshape(-1, w.num_splits)[rows, s], r["l"], rtol=1e-3)
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 16])
+@pytest.mark.parametrize("S", [1, 2, 3, 16, 17, 40])  # <= 16 and > 16 take different combine kernels
 @pytest.mark.parametrize("shape", [(2, 8, 2, 1, 1000, 128), (1, 4, 4, 2, 517, 64), (2, 8, 1, 1, 300, 32),
                                    (1, 4, 2, 40, 700, 128)])
 def test_splitkv_matches_unsplit(S, shape):
@@ -295,6 +295,23 @@ def test_splitkv_matches_unsplit(S, shape):
     assert np.allclose(mp[fin], rmp[fin], rtol=1e-3, atol=1e-3)
     assert np.allclose(lp[fin], rlp[fin], rtol=2e-3, atol=0)
     assert np.max(np.abs(op - rop)) < BF16_MAX
+
+
+def test_splitkv_mfma_rows_outside_a_split():
+    # Enough query rows per K/V head for the MFMA kernel in split mode; with
+    # a 100-key causal window most splits hold no key of a given row (on
+    # either side of its window), which must give (m, l, O) = (-inf, 0, 0).
+    inp = rand_inputs(1, 4, 1, 64, 2048, 128, seed=33, dtype="bf16")
+    o, lse, (op, mp, lp) = run_split(inp, 8, 1.0 / math.sqrt(128), causal=True, window=100)
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], 1.0 / math.sqrt(128), causal=True, window=100)
+    check_o(o, ref["o"], "bf16", "mfma split, window")
+    check_lse(lse, ref["lse"], "bf16", "mfma split, window")
+    rop, rmp, rlp = oracle.split_partials(inp["q"], inp["k"], inp["v"], 1.0 / math.sqrt(128), 8, causal=True,
+                                          window=100)
+    fin = np.isfinite(rmp)
+    assert (~fin).sum() > 0 and np.array_equal(fin, np.isfinite(mp))
+    assert np.all(lp[~fin] == 0) and np.all(op[~fin] == 0)
+    assert np.allclose(lp[fin], rlp[fin], rtol=2e-3, atol=0)
 
 
 def test_splitkv_window_and_empty_splits():
