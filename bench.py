@@ -347,7 +347,7 @@ PROFILE_RUNS = {
                        "python bench.py --copy-calibration",
 }
 KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
-           "combine": "combine_kernel<128>", "prefill_fp8": "fwd_fp8_kernel<128>",
+           "combine": "combine_few_kernel<128, 16>", "prefill_fp8": "fwd_fp8_kernel<128>",
            "rolling_decode": "splitkv_decode_kernel<128, 4, false>", "kv_append": "kv_append_kernel<128>",
            "softmax": "softmax_kernel<false, 4>", "topk": "softmax_topk_kernel<false, 4>",
            "copy": "__amd_rocclr_copyBuffer"}
@@ -458,7 +458,7 @@ of K and V by the 16 query tiles of each head are served from L2 / MALL.
     split_bytes = wl.algorithmic_bytes(wd) - part_bytes - (wd.B * wd.H * wd.Nq * (wd.d * 2 + 4))
     rb, wb = hbm["decode"]
     crb, cwb = hbm["combine"]
-    md = f"""# splitkv_decode_kernel + combine_kernel on the split-KV decode workload (B=16, H=32, Hkv=8, Nq=1, Nk=32768, d=128, 16 splits, bf16)
+    md = f"""# splitkv_decode_kernel + combine_few_kernel on the split-KV decode workload (B=16, H=32, Hkv=8, Nq=1, Nk=32768, d=128, 16 splits, bf16)
 
 Command (run from the repository root on one MI355X):
 

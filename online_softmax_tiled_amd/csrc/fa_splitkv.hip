@@ -331,13 +331,74 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ o
     if (lse && lane == 0) lse[row] = Lsum > 0.0f ? M + logf(Lsum) : kNegInf;
 }
 
+// Few splits (S <= SF): every load of the row is issued at once -- lane s
+// takes (m_s, l_s), and each lane the partial outputs of all S splits for
+// its columns -- so the merge costs one memory round trip instead of three.
+// Same arithmetic, in the same order, as combine_kernel: M over non-empty
+// splits, w_s = exp(m_s - M) l_s (lane s), l = the wave sum of w, and
+// O[d] = sum_s w_s O_s[d] / l with w_s broadcast from lane s.
+template <int D, int SF>
+__global__ __launch_bounds__(64) void combine_few_kernel(const float *__restrict__ o_part,
+                                                         const float *__restrict__ m_part,
+                                                         const float *__restrict__ l_part, void *o, float *lse,
+                                                         const int S, const int out_bf16) {
+    constexpr int PER = D >= 64 ? D / 64 : 1;
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    float ms = kNegInf, ls = 0.0f;
+    if (lane < S) {
+        ms = m_part[row * S + lane];
+        ls = l_part[row * S + lane];
+    }
+    float x[SF][PER];
+    const float *os = o_part + row * S * D;
+#pragma unroll
+    for (int s = 0; s < SF; ++s)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int dd = lane + 64 * k;
+            x[s][k] = (s < S && dd < D) ? os[s * D + dd] : 0.0f;
+        }
+    const float M = wave_max(ls > 0.0f ? ms : kNegInf);
+    const float w = (M != kNegInf && ls > 0.0f) ? expf(ms - M) * ls : 0.0f;
+    const float Lsum = M != kNegInf ? wave_sum(w) : 0.0f;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+    // Splits s >= S have w = 0 and x = 0: their FMAs leave acc unchanged.
+#pragma unroll
+    for (int s = 0; s < SF; ++s) {
+        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s));
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = fmaf(ws, x[s][k], acc[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int dd = lane + 64 * k;
+        if (dd >= D) continue;
+        const float val = Lsum > 0.0f ? acc[k] / Lsum : 0.0f;
+        if (out_bf16) {
+            const uint32_t wb = pack_bf16x2(val, 0.0f);
+            static_cast<uint16_t *>(o)[row * D + dd] = (uint16_t)(wb & 0xffffu);
+        } else {
+            static_cast<float *>(o)[row * D + dd] = val;
+        }
+    }
+    if (lse && lane == 0) lse[row] = Lsum > 0.0f ? M + logf(Lsum) : kNegInf;
+}
+
 template <int D>
 int launch_combine_d(const float *o_part, const float *m_part, const float *l_part, void *o, float *lse,
                      int64_t rows, int S, int out_dtype, hipStream_t stream) {
     if (rows == 0) return FA_OK;
     if (rows > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)rows), dim3(64), 0, stream, o_part, m_part, l_part, o, lse,
-                       S, out_dtype == FA_DTYPE_BF16 ? 1 : 0);
+    const int ob = out_dtype == FA_DTYPE_BF16 ? 1 : 0;
+    if (S <= 16)
+        hipLaunchKernelGGL((combine_few_kernel<D, 16>), dim3((unsigned)rows), dim3(64), 0, stream, o_part, m_part,
+                           l_part, o, lse, S, ob);
+    else
+        hipLaunchKernelGGL(combine_kernel<D>, dim3((unsigned)rows), dim3(64), 0, stream, o_part, m_part, l_part, o,
+                           lse, S, ob);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
