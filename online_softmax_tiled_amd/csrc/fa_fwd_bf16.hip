@@ -48,7 +48,10 @@
 //     more than TAU (log2 units).  Any reference point gives the same exact
 //     result (the merge rule rescales consistently); this one keeps the
 //     weights <= 2^TAU and makes the rescale of the output, a multiply of
-//     every accumulator, rare.
+//     every accumulator, rare;
+//   * the normaliser is the sum of the fp32 weights, taken before they are
+//     rounded to bf16 for P.V, so lse keeps fp32 accuracy however few keys
+//     a row sees.
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_tile.h"
@@ -108,7 +111,8 @@ struct Wave {
     using L = Smem<D>;
     bf16x8 qf[RB][D / 16];      // Q^T operand, per row block
     f32x16 oacc[RB][D / 32];    // O^T accumulators
-    float m[RB], l[RB];         // lazy reference max (log2 units); this lane's half of the sum
+    float m[RB], l[RB];         // lazy reference max (log2 units); this lane's half of the normaliser
+                                // (fp32 weights; FIXED: the bf16 weights P.V uses)
     float lx[RB];               // FIXED: this lane's half of the sum of the fp32 weights (for lse)
     float mtrue[RB];            // exact running max (log2 units)
     int lo_rel[RB], hi_rel[RB]; // visible keys relative to the first tile
@@ -231,9 +235,18 @@ struct Wave {
                 for (int j = 0; j < 16; ++j)
                     sacc[r][kb][j] = EXPLICIT ? fast_exp2(sacc[r][kb][j] - m_use)
                                               : fast_exp2(fmaf(sacc[r][kb][j], c_log2, -m_use));
-            // The row sum of these weights is added in the next matrix phase
-            // (from the bf16 weights P.V uses); here only the rescale.
-            l[r] *= alpha[r];
+            // The normaliser sums the fp32 weights, before their rounding to
+            // bf16 for P.V: a dominant weight's rounding (up to 2^-8 of it)
+            // would otherwise reach lse whole when a row sees few keys.
+            {
+                float rs[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rs[i] = (sacc[r][i / 4][4 * (i % 4)] + sacc[r][i / 4][4 * (i % 4) + 1]) +
+                            (sacc[r][i / 4][4 * (i % 4) + 2] + sacc[r][i / 4][4 * (i % 4) + 3]);
+                l[r] = fmaf(l[r], alpha[r],
+                            ((rs[0] + rs[1]) + (rs[2] + rs[3])) + ((rs[4] + rs[5]) + (rs[6] + rs[7])));
+            }
             // k-step (kb, gp) covers keys kb*32 + 16*gp + [0, 16): this lane
             // half supplies keys +4*hf+[0,4) and +8+4*hf+[0,4), which are
             // exactly accumulator elements 8*gp .. 8*gp+7.
@@ -266,11 +279,12 @@ struct Wave {
     template <bool SCHED = true>
     __device__ __forceinline__ void pv(const uint16_t *vt, const bf16x8 (&pf)[RB][4]) {
         const char *Vtb = reinterpret_cast<const char *>(vt);
-        // Row sum of this lane's 32 bf16 weights (dot2 with (1, 1)); the
-        // partner lane's half is added once, in the epilogue.
+        // FIXED: row sum of this lane's 32 bf16 weights (dot2 with (1, 1)),
+        // which normalises O; the partner lane's half is added once, in the
+        // epilogue.  The running-maximum path sums fp32 weights in softmax.
         const bf16x2 ones = as_bf16x2(0x3f803f80u);
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
+        for (int r = 0; r < (FIXED ? RB : 0); ++r) {
             float rs = 0.0f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

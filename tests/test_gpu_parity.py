@@ -4,7 +4,9 @@ Inputs come from the seeded generators in online_softmax_tiled_amd.workloads;
 the same bf16/fp32 values go to both sides.  Tolerances:
   * fp32 paths: max |O_gpu - O_oracle| <= 1e-5, |lse| error <= 1e-5 * max(1, |lse|);
   * bf16 paths: max abs error <= 2e-2 and mean abs error <= 2e-3 on O,
-    |lse| error <= 1e-3 * max(1, |lse|).
+    |lse| error <= 1e-4 * max(1, |lse|) (every bf16 path sums the fp32 weights
+    into the normaliser, so lse carries no bf16 rounding; the partial sums
+    are held to the same relative bound).
 Full-size workloads are checked on sampled rows the oracle computes one by
 one, in the launch configuration the benchmark times.
 """
@@ -22,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 FP32_TOL = 1e-5
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+BF16_LSE = 1e-4
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -61,7 +64,7 @@ def check_lse(lse_gpu, lse_ref, dtype, what=""):
     fin = np.isfinite(lse_ref)
     assert np.array_equal(fin, np.isfinite(lse_gpu)), f"{what}: -inf pattern differs"
     assert np.all(lse_gpu[~fin] == -np.inf)
-    rel = (FP32_TOL if dtype == "fp32" else 1e-3)
+    rel = (FP32_TOL if dtype == "fp32" else BF16_LSE)
     err = np.abs(lse_gpu[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))
     assert err.size == 0 or err.max() <= rel, f"{what}: lse rel err {err.max():.3g}"
 
@@ -273,7 +276,7 @@ def test_splitkv_decode_workload_full():
                              key_range=(s * chunk, min(w.Nk, (s + 1) * chunk)))
         assert np.max(np.abs(op.reshape(-1, w.num_splits, w.d)[rows, s] - r["o"])) < BF16_MAX
         assert np.allclose(mp.reshape(-1, w.num_splits)[rows, s], r["m"], rtol=1e-3, atol=1e-3)
-        assert np.allclose(lp.reshape(-1, w.num_splits)[rows, s], r["l"], rtol=1e-3)
+        assert np.allclose(lp.reshape(-1, w.num_splits)[rows, s], r["l"], rtol=BF16_LSE)
 
 
 @pytest.mark.parametrize("S", [1, 2, 3, 16, 17, 40])  # <= 16 and > 16 take different combine kernels
@@ -293,7 +296,7 @@ def test_splitkv_matches_unsplit(S, shape):
     fin = np.isfinite(rmp)
     assert np.array_equal(fin, np.isfinite(mp)) and np.all(lp[~fin] == 0)
     assert np.allclose(mp[fin], rmp[fin], rtol=1e-3, atol=1e-3)
-    assert np.allclose(lp[fin], rlp[fin], rtol=2e-3, atol=0)
+    assert np.allclose(lp[fin], rlp[fin], rtol=BF16_LSE, atol=0)
     assert np.max(np.abs(op - rop)) < BF16_MAX
 
 
@@ -311,7 +314,7 @@ def test_splitkv_mfma_rows_outside_a_split():
     fin = np.isfinite(rmp)
     assert (~fin).sum() > 0 and np.array_equal(fin, np.isfinite(mp))
     assert np.all(lp[~fin] == 0) and np.all(op[~fin] == 0)
-    assert np.allclose(lp[fin], rlp[fin], rtol=2e-3, atol=0)
+    assert np.allclose(lp[fin], rlp[fin], rtol=BF16_LSE, atol=0)
 
 
 def test_splitkv_window_and_empty_splits():

@@ -70,3 +70,38 @@ def test_fp8_random_shapes(seed):
     print("case", what, flush=True)
     make = t8.narrow_inputs if family == "narrow" else t8.random_inputs
     t8.check(make(B, H, Hkv, Nq, Nk, d, seed=seed), 1.0 / math.sqrt(d), causal, window, what)
+
+
+@pytest.mark.parametrize("seed", range(14))
+def test_splitkv_random_shapes(seed):
+    # Few rows per K/V head take the decode kernel (1, 2 or 4 rows per
+    # pass), more take the MFMA kernel in split mode; up to 16 splits and
+    # more take different combine kernels.
+    rng = np.random.default_rng(4000 + seed)
+    Hkv = int(rng.choice([1, 2, 4]))
+    H = Hkv * int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 3))
+    Nk = int(rng.integers(1, 3000))
+    Nq = int(rng.choice([1, 1, 2, int(rng.integers(3, 70))]))
+    d = int(rng.choice([32, 64, 128]))
+    S = int(rng.choice([1, 2, 5, 16, 17, 40]))
+    causal = rng.random() < 0.5
+    window = int(rng.integers(1, 400)) if causal and rng.random() < 0.5 else 0
+    softcap = float(rng.choice([0.0, 0.0, 30.0]))
+    scale = 1.0 / math.sqrt(d)
+    what = (f"split seed={seed} B={B} H={H} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} S={S} causal={causal} W={window} "
+            f"cap={softcap}")
+    print("case", what, flush=True)
+    inp = tp.rand_inputs(B, H, Hkv, Nq, Nk, d, seed=seed, dtype="bf16")
+    kw = dict(causal=causal, window=window, softcap=softcap)
+    o, lse, (op, mp, lp) = tp.run_split(inp, S, scale, **kw)
+    ref = tp.oracle.attention(inp["q"], inp["k"], inp["v"], scale, **kw)
+    tp.check_o(o, ref["o"], "bf16", what)
+    tp.check_lse(lse, ref["lse"], "bf16", what)
+    rop, rmp, rlp = tp.oracle.split_partials(inp["q"], inp["k"], inp["v"], scale, S, **kw)
+    fin = np.isfinite(rmp)
+    assert np.array_equal(fin, np.isfinite(mp)), what
+    assert np.all(lp[~fin] == 0) and np.all(op[~fin] == 0), what
+    assert np.allclose(mp[fin], rmp[fin], rtol=1e-3, atol=1e-3), what
+    assert np.allclose(lp[fin], rlp[fin], rtol=tp.BF16_LSE, atol=0), what
+    assert np.max(np.abs(op - rop), initial=0.0) < tp.BF16_MAX, what

@@ -22,6 +22,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+BF16_LSE = 1e-4  # lse relative bound (the normaliser sums fp32 weights)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -79,7 +80,7 @@ def check_decode(cache, inp, pos, window, sinks, scale, softcap, S, what):
     assert np.all(np.isfinite(host(o))), what
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, f"{what}: err max {err.max():.3g} mean {err.mean():.3g}"
     lerr = np.abs(host(lse) - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))
-    assert lerr.max() <= 1e-3, f"{what}: lse rel err {lerr.max():.3g}"
+    assert lerr.max() <= BF16_LSE, f"{what}: lse rel err {lerr.max():.3g}"
 
 
 # B, H, Hkv, d, window, sinks, prefill chunk, positions checked, num_splits, softcap
@@ -155,4 +156,4 @@ def test_rolling_bench_shape_sampled():
         ref = oracle.attention(q[b:b + 1], kc[b:b + 1], vc[b:b + 1], 1.0 / math.sqrt(d))
         err = np.abs(host(o)[b:b + 1] - ref["o"])
         assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
-        assert np.allclose(host(lse)[b:b + 1], ref["lse"], rtol=1e-3, atol=1e-3)
+        assert np.allclose(host(lse)[b:b + 1], ref["lse"], rtol=BF16_LSE, atol=BF16_LSE)
