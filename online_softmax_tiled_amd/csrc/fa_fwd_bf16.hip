@@ -427,18 +427,18 @@ __global__ __launch_bounds__(NT, 1) void fwd_bf16_kernel(const FwdParams p, cons
         k_goff[u] = (rr * D + L::kslot(rr, sl) * 8) * 2;
         v_goff[u] = (rr * D + L::vslot(rr, sl) * 8) * 2;
     }
-    const int head_bytes = (int)(Nk * D * 2);
+    const uint32_t head_bytes = (uint32_t)(Nk * D * 2);
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
     const int kt0 = (int)kbeg;
 
     auto load_k = [&](int t, uint16_t *buf) {
-        const int toff = (kt0 + t * BN) * D * 2;
+        const uint32_t toff = (uint32_t)(kt0 + t * BN) * (uint32_t)(D * 2);
 #pragma unroll
         for (int u = 0; u < L::LPW; ++u)
             buffer_load_lds16(K, head_bytes, (lds_void *)(buf + (lw * L::LPW + u) * 64 * 8), k_goff[u], toff);
     };
     auto load_v = [&](int t, uint16_t *buf) {  // buf: vstage
-        const int toff = (kt0 + t * BN) * D * 2;
+        const uint32_t toff = (uint32_t)(kt0 + t * BN) * (uint32_t)(D * 2);
 #pragma unroll
         for (int u = 0; u < L::LPW; ++u)
             buffer_load_lds16(V, head_bytes, (lds_void *)(buf + (lw * L::LPW + u) * 64 * 8), v_goff[u], toff);

@@ -338,18 +338,18 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(const FwdParams p, const
     const uint32_t sel_lo = c0 | ((4 + c0) << 8) | (c1 << 16) | ((4 + c1) << 24);
     const uint32_t sel_hi = c2 | ((4 + c2) << 8) | (c3 << 16) | ((4 + c3) << 24);
 
-    const int head_bytes = (int)(Nk * D);
+    const uint32_t head_bytes = (uint32_t)(Nk * D);
     const int ntiles = kend > kbeg ? (int)((kend - kbeg + BN - 1) / BN) : 0;
     const int kt0 = (int)kbeg;
 
     auto load_k = [&](int t, uint8_t *buf) {
-        const int toff = (kt0 + t * BN) * D;
+        const uint32_t toff = (uint32_t)(kt0 + t * BN) * (uint32_t)D;
 #pragma unroll
         for (int u = 0; u < L::LPW; ++u)
             buffer_load_lds16(K, head_bytes, (lds_void *)(buf + (lw * L::LPW + u) * 1024), k_goff[u], toff);
     };
     auto load_v = [&](int t) {
-        const int toff = (kt0 + t * BN) * D;
+        const uint32_t toff = (uint32_t)(kt0 + t * BN) * (uint32_t)D;
 #pragma unroll
         for (int u = 0; u < L::LPW; ++u)
             buffer_load_lds16(V, head_bytes, (lds_void *)(vstage + (lw * L::LPW + u) * 1024), v_goff[u], toff);

@@ -12,7 +12,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from base + voff + soff straight into LDS (dst + 16*lane).
 // The buffer resource bounds the access to [base, base + nbytes): bytes past
-// the end read as zero.  base, nbytes, dst and soff are wave-uniform.
+// the end read as zero.  base, nbytes, dst and soff are wave-uniform; nbytes
+// and soff are unsigned 32-bit byte counts (a head of K or V is at most
+// 2^31 - 1 elements, so up to 2^32 - 2 bytes in bf16).
 //
 // Written as inline assembly so that the compiler does not see an LDS write
 // in flight: it would otherwise wait for every such load to land before the
@@ -20,12 +22,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // (s_waitcnt vmcnt) before the barrier that hands the tile to other waves.
 // The instruction has no result register; M0 (the LDS address) is saved and
 // restored around it.
-__device__ __forceinline__ void buffer_load_lds16(const void *base, int nbytes, lds_void *dst, int voff, int soff) {
+__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t nbytes, lds_void *dst, int voff,
+                                                  uint32_t soff) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     u32x4 rsrc;
     rsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
     rsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);  // stride 0
-    rsrc[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);               // num_records
+    rsrc[2] = __builtin_amdgcn_readfirstlane(nbytes);                         // num_records
     rsrc[3] = 0x00020000u;                                                    // raw buffer, dword data
     const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(dst));
     uint32_t saved;
