@@ -3,8 +3,13 @@ batch, head group, query and key lengths (ragged against the 256-row query
 tiles and 64-key tiles), head size, causal / window / soft-cap choices.
 Tolerances are those of tests/test_gpu_parity.py (bf16, fp32) and
 tests/test_gpu_fp8.py (fp8 bounds from E4M3 rounding and the fp8
-instruction's accumulation)."""
+instruction's accumulation).
+
+FA_RANDOM_SHAPES_SCALE=k multiplies the number of seeds of every family (a
+longer sweep: k = 125 runs 1500 bf16, 1500 fp8, 1750 split-KV and 750 fp32
+cases in a few minutes on one MI355X)."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -15,6 +20,8 @@ import test_gpu_parity as tp
 torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
+
+SCALE = max(1, int(os.environ.get("FA_RANDOM_SHAPES_SCALE", "1")))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -39,7 +46,7 @@ def draw_shape(rng, ds):
     return B, H, Hkv, Nq, Nk, d, causal, window
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(12 * SCALE))
 def test_bf16_random_shapes(seed):
     rng = np.random.default_rng(1000 + seed)
     B, H, Hkv, Nq, Nk, d, causal, window = draw_shape(rng, [32, 64, 128])
@@ -50,7 +57,7 @@ def test_bf16_random_shapes(seed):
     tp.parity(inp, "bf16", 1.0 / math.sqrt(d), causal=causal, window=window, softcap=softcap, what=what)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(6 * SCALE))
 def test_fp32_random_shapes(seed):
     rng = np.random.default_rng(2000 + seed)
     B, H, Hkv, Nq, Nk, d, causal, window = draw_shape(rng, [32, 64, 128])
@@ -60,7 +67,7 @@ def test_fp32_random_shapes(seed):
     tp.parity(inp, "fp32", 1.0 / math.sqrt(d), causal=causal, window=window, what=what)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(10 * SCALE))
 def test_fp8_random_shapes(seed):
     rng = np.random.default_rng(3000 + seed)
     B, H, Hkv, Nq, Nk, d, causal, window = draw_shape(rng, [64, 128])
@@ -72,7 +79,7 @@ def test_fp8_random_shapes(seed):
     t8.check(make(B, H, Hkv, Nq, Nk, d, seed=seed), 1.0 / math.sqrt(d), causal, window, what)
 
 
-@pytest.mark.parametrize("seed", range(14))
+@pytest.mark.parametrize("seed", range(14 * SCALE))
 def test_splitkv_random_shapes(seed):
     # Few rows per K/V head take the decode kernel (1, 2 or 4 rows per
     # pass), more take the MFMA kernel in split mode; up to 16 splits and
