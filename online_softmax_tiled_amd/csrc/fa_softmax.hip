@@ -17,7 +17,8 @@
 // when a value exceeds it by more than TAU, so each term is <= e^TAU); the
 // lanes' states are merged with the two-block rule of Transformers & Math
 // section 16.2 (d = e^(m1-m) d1 + e^(m2-m) d2).  Exponentials are exp2 of
-// fma(x, log2 e, -m log2 e).
+// (x - m) log2 e: the difference first, so that rounding a large reference
+// m log2 e does not reach every weight.
 //
 // Top-k: every wave keeps a sorted list of its k best (value, column) pairs
 // spread over its lanes (lane j holds the j-th best, j < k <= 64).  A loaded
@@ -104,9 +105,11 @@ struct Norm {
         const float mn = mx > m + TAU ? mx : m;  // move the reference only by more than TAU
         const float mu = mn == kNegInf ? 0.0f : mn;
         float s = d * fast_exp2((m - mu) * kLog2e);
-        const float ml = mu * kLog2e;
+        // x - mu first: exact for the values that carry weight (Sterbenz),
+        // so the error does not grow with |x| as a rounded mu * log2(e)
+        // reference would make it (2^-24 |mu| log2(e) in every exponent).
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) s += fast_exp2(fmaf(x[i], kLog2e, -ml));
+        for (int i = 0; i < EPV; ++i) s += fast_exp2((x[i] - mu) * kLog2e);
         m = mn;
         d = s;
     }
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(NT_SOFTMAX) void softmax_kernel(const void *x, void
         for (int u = 0; u < UNROLL; ++u) s.add<EPV>(xv[u]);
     }
     const Norm t = block_norm<NWAVE>(s, sm, sd);
-    const float ml = (t.m == kNegInf ? 0.0f : t.m) * kLog2e;
+    const float mref = t.m == kNegInf ? 0.0f : t.m;
     const float inv = 1.0f / t.d;
     if (lse && tid == 0) lse[r] = t.m + __logf(t.d);
 
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(NT_SOFTMAX) void softmax_kernel(const void *x, void
             if (v < nvec) {
                 float yv[EPV];
 #pragma unroll
-                for (int i = 0; i < EPV; ++i) yv[i] = fast_exp2(fmaf(xv[u][i], kLog2e, -ml)) * inv;
+                for (int i = 0; i < EPV; ++i) yv[i] = fast_exp2((xv[u][i] - mref) * kLog2e) * inv;
                 store_vec<BF16, EPV>(yr, v * EPV, yv);
             }
         }
@@ -343,8 +346,8 @@ __global__ __launch_bounds__(NT_TOPK) void softmax_topk_kernel(const void *x, fl
         }
     }
     if (lane < k) {
-        const float ml = (t.m == kNegInf ? 0.0f : t.m) * kLog2e;
-        probs[r * k + lane] = fast_exp2(fmaf(top.lv, kLog2e, -ml)) / t.d;
+        const float mref = t.m == kNegInf ? 0.0f : t.m;
+        probs[r * k + lane] = fast_exp2((top.lv - mref) * kLog2e) / t.d;
         idx[r * k + lane] = top.li;
     }
     if (lse && lane == 0) lse[r] = t.m + __logf(t.d);

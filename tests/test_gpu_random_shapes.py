@@ -5,6 +5,10 @@ Tolerances are those of tests/test_gpu_parity.py (bf16, fp32) and
 tests/test_gpu_fp8.py (fp8 bounds from E4M3 rounding and the fp8
 instruction's accumulation).
 
+Also: token streams through a rolling KV cache (random window, sinks, chunk
+sizes and check positions) and row softmax / fused top-k over random row
+lengths, both with the tolerances of their own test files.
+
 FA_RANDOM_SHAPES_SCALE=k multiplies the number of seeds of every family (a
 longer sweep: k = 125 runs 1500 bf16, 1500 fp8, 1750 split-KV and 750 fp32
 cases in a few minutes on one MI355X)."""
@@ -16,6 +20,8 @@ import pytest
 
 import test_gpu_fp8 as t8
 import test_gpu_parity as tp
+import test_gpu_rolling as tr
+import test_gpu_softmax as tsm
 
 torch = pytest.importorskip("torch")
 
@@ -112,3 +118,51 @@ def test_splitkv_random_shapes(seed):
     assert np.allclose(mp[fin], rmp[fin], rtol=1e-3, atol=1e-3), what
     assert np.allclose(lp[fin], rlp[fin], rtol=tp.BF16_LSE, atol=0), what
     assert np.max(np.abs(op - rop), initial=0.0) < tp.BF16_MAX, what
+
+
+@pytest.mark.parametrize("seed", range(8 * SCALE))
+def test_rolling_random_streams(seed):
+    rng = np.random.default_rng(5000 + seed)
+    Hkv = int(rng.choice([1, 2, 4]))
+    H = Hkv * int(rng.choice([1, 2, 4, 16]))
+    B = int(rng.integers(1, 3))
+    d = int(rng.choice([32, 64, 128]))
+    W = int(rng.integers(1, 200))
+    S = int(rng.choice([0, 1, 4]))
+    nsplit = int(rng.choice([1, 2, 3, 5, 17]))
+    cap = float(rng.choice([0.0, 0.0, 30.0]))
+    N = int(rng.integers(1, 500))
+    pre = int(rng.integers(1, N + 1))
+    checks = sorted(set([pre - 1, N - 1] + [int(x) for x in rng.integers(pre - 1, N, 3)]))
+    what = f"rolling seed={seed} B={B} H={H} Hkv={Hkv} d={d} W={W} sinks={S} N={N} pre={pre} S={nsplit} cap={cap}"
+    print("case", what, flush=True)
+    inp = tr.seq_inputs(B, H, Hkv, N, d, seed=seed)
+    k_all, v_all = tr.dev(inp["k"]), tr.dev(inp["v"])
+    cache = tr.fa_mod().RollingKVCache(B, Hkv, d, W, S)
+    scale = 1.0 / math.sqrt(d)
+    pos = -1
+    while pos < checks[-1]:
+        T = pre if pos < 0 else int(rng.integers(1, 4))
+        T = min(T, N - 1 - pos)
+        cache.append(k_all[:, :, pos + 1:pos + 1 + T].contiguous(), v_all[:, :, pos + 1:pos + 1 + T].contiguous())
+        pos += T
+        if pos in checks:
+            tr.check_decode(cache, inp, pos, W, S, scale, cap, nsplit, f"{what} pos={pos}")
+    torch.cuda.synchronize()
+    tr.check_cache(cache, inp["k"], inp["v"], pos, W, S)
+
+
+@pytest.mark.parametrize("seed", range(8 * SCALE))
+def test_softmax_random_rows(seed):
+    rng = np.random.default_rng(6000 + seed)
+    dtype = str(rng.choice(["fp32", "bf16"]))
+    rows = int(rng.integers(1, 9))
+    n = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 40000)), int(rng.integers(40000, 300000))]))
+    scale = float(rng.choice([1e-3, 1.0, 3.0, 30.0]))
+    shift = float(rng.choice([0.0, -200.0, 500.0]))
+    k = int(rng.integers(1, min(64, n) + 1))
+    what = f"softmax seed={seed} {dtype} rows={rows} n={n} scale={scale} shift={shift} k={k}"
+    print("case", what, flush=True)
+    x = tsm.logits(rows, n, seed=seed, dtype=dtype, scale=scale, shift=shift)
+    tsm.check_softmax(x, dtype, what)
+    tsm.check_topk(x, dtype, k, what)
