@@ -78,6 +78,11 @@ typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
  * usual scaled dot product, nx_flashattn_scale.nx and Transformers & Math
  * section 16.5).  causal: 0/1.  window: 0 = none, > 0 needs causal.
  * softcap: 0 = none, > 0 = cap value.
+ * Numerics: scores, the running maximum, the normaliser and O accumulate in
+ * fp32; each tile's weights are rounded to bf16 for the P.V product, while
+ * the normaliser, and so lse, sums the fp32 weights.  (With a soft-cap up to
+ * 60 the reference maximum stays 0; O is then divided by the sum of the
+ * bf16 weights P.V used, lse still takes the fp32 sum.)
  * Errors: FA_ERR_INVALID_ARG for negative sizes, Hkv < 1, H % Hkv != 0, a
  * NULL q/k/v/o when the tensor is non-empty, window < 0, window > 0 without
  * causal, softcap < 0 or non-finite, non-finite scale; FA_ERR_UNSUPPORTED
