@@ -133,6 +133,42 @@ def bench_prefill(torch, fa, steps, warmup):
     }
 
 
+# Other prefill configurations reported beside the headline one (TFLOP/s and
+# fraction of the bf16 peak): non-causal small heads, and causal GQA with
+# sliding windows on even heads and a soft-cap (the fixed-maximum kernel).
+OTHER_PREFILL = ("bf16_b1_h8_n1024_d64", "bf16_gqa_swa_softcap_h32kv8_n16384_d128")
+
+
+def bench_prefill_config(torch, fa, name, steps, warmup):
+    w = wl.WORKLOADS[name]
+    t = to_device(wl.generate(w), torch)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    hw = list(w.head_window) if w.head_window else None
+    # The argument block is built once (the smaller workload's launches take
+    # tens of microseconds; rebuilding it per launch would time the host).
+    import ctypes
+    from online_softmax_tiled_amd.fa import FwdArgs
+    hw_arr = (ctypes.c_int32 * len(hw))(*hw) if hw else None
+    a = FwdArgs(0, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, float(w.scale), int(w.causal), int(w.window),
+                   float(w.softcap), ctypes.cast(hw_arr, ctypes.POINTER(ctypes.c_int32)) if hw else None,
+                   torch.cuda.current_stream().cuda_stream or None)
+    lib, ref = fa.load_library(), ctypes.byref(a)
+
+    def launch():
+        if lib.fa_fwd_ex(ref) != 0:
+            raise RuntimeError("fa_fwd_ex failed")
+
+    avg, total, wall = time_launches(launch, steps, warmup, torch)
+    flops = wl.algorithmic_flops(w)
+    value = flops * steps / (total * 1e-3) / 1e12
+    return {"workload": name, "value": round(value, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(total / steps, 4), "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+            "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                       "head_window": "W on even heads" if hw else None, "softcap": w.softcap or None}}
+
+
 def bench_prefill_fp8(torch, fa, steps, warmup):
     w = wl.FP8_PREFILL
     x = wl.generate_fp8(w)
@@ -346,7 +382,7 @@ PROFILE_RUNS = {
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
                        "python bench.py --copy-calibration",
 }
-KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
+KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false, 8>", "decode": "splitkv_decode_kernel<128, 4, false>",
            "combine": "combine_few_kernel<128, 16>", "prefill_fp8": "fwd_fp8_kernel<128>",
            "rolling_decode": "splitkv_decode_kernel<128, 4, false>", "kv_append": "kv_append_kernel<128>",
            "softmax": "softmax_kernel<false, 4>", "topk": "softmax_topk_kernel<false, 4>",
@@ -621,7 +657,7 @@ def main():
         print(json.dumps({"leg": args.workload, **r}), flush=True)
         return
     main_w, leg = None, None
-    decode = rolling = softmax = fp8 = None
+    decode = rolling = softmax = fp8 = others = None
     if args.workload == "prefill":
         main_w, leg = bench_prefill(torch, fa, args.steps, args.warmup)
         print(f"[bench] prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
@@ -636,6 +672,11 @@ def main():
                   f"{softmax['topk']['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
             _, fp8 = bench_prefill_fp8(torch, fa, args.steps, args.warmup)
             print(f"[bench] fp8 prefill done: {fp8['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
+            others = {}
+            for name in OTHER_PREFILL:
+                others[name] = bench_prefill_config(torch, fa, name, args.steps, args.warmup)
+                print(f"[bench] {name} done: {others[name]['ms_per_step']:.4f} ms/launch", file=sys.stderr,
+                      flush=True)
         value, unit = leg["value"], "TFLOP/s"
     elif args.workload == "prefill_fp8":
         main_w, leg = bench_prefill_fp8(torch, fa, args.steps, args.warmup)
@@ -671,6 +712,8 @@ def main():
         out["prefill_fp8"] = {"workload": w8.name, "value": round(fp8["value"], 2), "unit": "TFLOP/s",
                               "ms_per_step": round(fp8["total_ms"] / args.steps, 4), "dtype": "fp8 e4m3 (bf16 out)",
                               "roofline": fp8["roofline"]}
+    if others is not None:
+        out["other_prefill"] = others
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)
