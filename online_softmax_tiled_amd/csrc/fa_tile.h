@@ -100,7 +100,17 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
     const int units = (int)(p.B * p.Hkv);
     const int per_unit = rep * n_qtiles * S;
     int unit, r;
-    if (units % 8 == 0) {
+    if (units % 8 == 0 && p.causal) {
+        // Causal tiles differ in length: order each XCD's blocks by query
+        // tile, longest first across all its heads, so the short tiles fill
+        // in at the end (grouping by head, longest first within each head,
+        // left the last heads' long tiles in the tail).
+        const int x = bid & 7, s = bid >> 3;
+        const int per_rank = (units / 8) * rep * S;
+        const int rank = s / per_rank, rem = s % per_rank;
+        unit = (rem / (rep * S)) * 8 + x;
+        r = rank * (rep * S) + rem % (rep * S);
+    } else if (units % 8 == 0) {
         const int x = bid & 7, s = bid >> 3;
         unit = (s / per_unit) * 8 + x;
         r = s % per_unit;
