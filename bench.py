@@ -460,6 +460,7 @@ def summarize_profiles(d):
     name, calls, avg, mn, mx = stat(KERNELS["prefill"], "trace_prefill")
     flops = wl.algorithmic_flops(wp)
     rb, wb = hbm["prefill"]
+    qkv_bytes = 2 * (wp.B * wp.H * wp.Nq * wp.d + 2 * wp.B * wp.Hkv * wp.Nk * wp.d)
     md = f"""# fwd_bf16_kernel on the causal prefill workload (B=4, H=32, Nq=Nk=4096, d=128, bf16)
 
 Command (run from the repository root on one MI355X):
@@ -481,8 +482,10 @@ at the minimum, {flops / (mn * 1e-6) / 1e12:.0f} TFLOP/s.
 HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE,
 scaled by a 1 GiB copy; see hbm_traffic.json for the commands): read {rb / 1e6:.1f} MB,
 written {wb / 1e6:.1f} MB, total {(rb + wb) / 1e6:.1f} MB, against {wl.algorithmic_bytes(wp) / 1e6:.1f} MB of
-algorithmic bytes (Q, K, V read once, O and lse written once): the re-reads
-of K and V by the 16 query tiles of each head are served from L2 / MALL.
+algorithmic bytes (Q, K, V read once, O and lse written once).  Reads are
+{rb / qkv_bytes:.2f}x the {qkv_bytes / 1e6:.1f} MB of Q, K and V: most re-reads of a head's K and V by
+its {(wp.Nq + 255) // 256} query tiles hit in L2 / MALL, because each XCD works on a few heads at a
+time (blocks ordered longest tile first within clusters of heads).
 """
     with open(os.path.join(ROOT, "profiles", f"fwd_bf16_causal_b4_h32_n4096_d128.md"), "w") as f:
         f.write(md)

@@ -101,15 +101,26 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
     const int per_unit = rep * n_qtiles * S;
     int unit, r;
     if (units % 8 == 0 && p.causal) {
-        // Causal tiles differ in length: order each XCD's blocks by query
-        // tile, longest first across all its heads, so the short tiles fill
-        // in at the end (grouping by head, longest first within each head,
-        // left the last heads' long tiles in the tail).
+        // Causal tiles differ in length.  Each XCD takes its units in
+        // clusters of C; inside a cluster the blocks run longest query tile
+        // first across the cluster's units, so short tiles fill in at the
+        // end of each cluster (one unit at a time, longest first, left the
+        // last unit's long tiles in the tail).  C is the fewest units whose
+        // blocks reach twice the XCD's 32 resident workgroups: enough to
+        // balance, while only about C units' K and V are live in the XCD's
+        // L2 at a time (ordering across all units at once multiplied the
+        // HBM reads of K and V).
         const int x = bid & 7, s = bid >> 3;
-        const int per_rank = (units / 8) * rep * S;
-        const int rank = s / per_rank, rem = s % per_rank;
-        unit = (rem / (rep * S)) * 8 + x;
-        r = rank * (rep * S) + rem % (rep * S);
+        const int upx = units / 8;
+        const int unit_blocks = per_unit;
+        const int C = min(upx, max(1, (64 + unit_blocks - 1) / unit_blocks));
+        const int c0 = (s / (C * unit_blocks)) * C;
+        const int csz = min(C, upx - c0);
+        const int rem = s - c0 * unit_blocks;
+        const int per_rank = csz * rep * S;
+        const int rank = rem / per_rank, rr = rem % per_rank;
+        unit = (c0 + rr / (rep * S)) * 8 + x;
+        r = rank * (rep * S) + rr % (rep * S);
     } else if (units % 8 == 0) {
         const int x = bid & 7, s = bid >> 3;
         unit = (s / per_unit) * 8 + x;
