@@ -209,6 +209,20 @@ def _shapes(q, k, v):
     return B, H, Hkv, Nq, Nk, d
 
 
+def _buffer(t, shape, dtype, device, name):
+    """A caller-supplied output buffer: it must be a contiguous device tensor
+    of exactly this shape and dtype (the kernels write every element of it
+    and nothing past it)."""
+    import torch
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != shape or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {list(shape)}, "
+                         f"got {t.dtype} {list(t.shape)}")
+    return t
+
+
 def attention(q, k, v, scale=None, causal=False, window=0, head_window=None, softcap=0.0,
               out=None, lse=None):
     """O = softmax(scale * q k^T) v per head (exact, tiled).  q: [B,H,Nq,d],
@@ -222,8 +236,8 @@ def attention(q, k, v, scale=None, causal=False, window=0, head_window=None, sof
         dtype = FA_DTYPE_FP32
     else:
         raise ValueError("q, k, v must be bfloat16 or float32")
-    o = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _buffer(out, q.shape, q.dtype, q.device, "out")
+    lse = _buffer(lse, (B, H, Nq), torch.float32, q.device, "lse")
     if head_window is not None:
         fa_fwd_ex(dtype, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap,
                   head_window=head_window)
@@ -244,8 +258,8 @@ def attention_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, scale=No
         raise ValueError("q, k, v must be float8_e4m3fn or uint8 (E4M3 bytes)")
     B, H, Hkv, Nq, Nk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None else out
-    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _buffer(out, (B, H, Nq, d), torch.bfloat16, q.device, "out")
+    lse = _buffer(lse, (B, H, Nq), torch.float32, q.device, "lse")
     fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale, causal, window)
     return o, lse
 
@@ -261,12 +275,10 @@ def splitkv_attention(q, k, v, num_splits, scale=None, causal=False, window=0, s
         raise ValueError("split-KV takes bfloat16 q, k, v")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     S = int(num_splits)
-    if partials is None:
-        o_part = torch.empty((B, H, Nq, S, d), dtype=torch.float32, device=q.device)
-        m_part = torch.empty((B, H, Nq, S), dtype=torch.float32, device=q.device)
-        l_part = torch.empty((B, H, Nq, S), dtype=torch.float32, device=q.device)
-    else:
-        o_part, m_part, l_part = partials
+    o_part, m_part, l_part = (None, None, None) if partials is None else partials
+    o_part = _buffer(o_part, (B, H, Nq, S, d), torch.float32, q.device, "o_part")
+    m_part = _buffer(m_part, (B, H, Nq, S), torch.float32, q.device, "m_part")
+    l_part = _buffer(l_part, (B, H, Nq, S), torch.float32, q.device, "l_part")
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)

@@ -207,3 +207,16 @@ def test_fp8_validation(over, status):
 
 def test_fp8_empty_is_a_no_op():
     assert call_fp8(Nq=0, q=None, o=None) == fa.FA_OK
+
+
+def test_binding_rejects_mis_sized_output_buffers():
+    # A caller-supplied output must match the shape and dtype the kernel
+    # writes, be contiguous and live on the device; the binding checks this
+    # before any launch (here on host tensors, which it also rejects).
+    torch = pytest.importorskip("torch")
+    good = fa._buffer(None, (2, 3), torch.float32, "cpu", "out")
+    assert tuple(good.shape) == (2, 3) and good.dtype == torch.float32
+    for bad in (torch.empty(2, 4), torch.empty(2, 3, dtype=torch.float64), torch.empty(3, 2).t(),
+                torch.empty(2, 3)):
+        with pytest.raises(ValueError, match="out must be"):
+            fa._buffer(bad, (2, 3), torch.float32, "cpu", "out")

@@ -75,8 +75,11 @@ def fa_mod():
 
 def run(x, scale, causal=False, window=0):
     dev = {n: torch.from_numpy(np.ascontiguousarray(x[n])).cuda() for n in "qkv"}
+    B, H, Nq, d = dev["q"].shape
+    o = torch.full((B, H, Nq, d), float("nan"), dtype=torch.bfloat16, device="cuda")  # unwritten -> fails
+    lse = torch.full((B, H, Nq), float("nan"), device="cuda")
     o, lse = fa_mod().attention_fp8(dev["q"], dev["k"], dev["v"], x["q_descale"], x["k_descale"],
-                                    x["v_descale"], scale=scale, causal=causal, window=window)
+                                    x["v_descale"], scale=scale, causal=causal, window=window, out=o, lse=lse)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -151,12 +154,14 @@ def check(x, scale, causal, window, what):
     o, lse = run(x, scale, causal, window)
     ref = oracle_fp8(x, scale, causal, window)
     rig, mean_elem, lse_b = bounds(x, scale, causal, window, ref)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     err = np.abs(o - ref["o"])
     bad = err > rig
     assert not bad.any(), f"{what}: {bad.sum()} elements beyond the rounding bound, worst {np.max(err - rig):.3g}"
     assert err.mean() <= mean_elem.mean() + 1e-7, f"{what}: mean error {err.mean():.3g} > {mean_elem.mean():.3g}"
     fin = np.isfinite(ref["lse"])
     assert np.array_equal(np.isfinite(lse), fin), f"{what}: rows with no visible key"
+    assert np.all(lse[~fin] == -np.inf), f"{what}: lse of a row with no visible key must be -inf"
     dl = np.abs(lse[fin] - ref["lse"][fin])
     assert np.all(dl <= lse_b[fin]), f"{what}: lse, worst excess {np.max(dl - lse_b[fin]):.3g}"
     assert np.all(o[~fin] == 0.0), f"{what}: rows with no visible key must be 0"
@@ -285,6 +290,8 @@ def test_fp8_full_size_prefill_sampled():
     print(f"case fp8 full size {w.name}", flush=True)
     x = wl.generate_fp8(w)
     o, lse = run(x, w.scale, w.causal, w.window)
+    # Every row sees at least its own key: all of O and lse is written.
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     rng = np.random.default_rng(0)
     Nq = w.Nq
     picks = {0, 1, 255, 256, 257, Nq - 1, Nq - 2, Nq - 256, 4 * Nq + 4095, (w.B * w.H - 1) * Nq + 1000}

@@ -72,8 +72,11 @@ def check_lse(lse_gpu, lse_ref, dtype, what=""):
 def run_gpu(inp, dtype, scale, causal=False, window=0, head_window=None, softcap=0.0):
     tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
     q, k, v = dev(inp["q"], tdt), dev(inp["k"], tdt), dev(inp["v"], tdt)
+    # Outputs start as NaN: an element the kernel does not write fails.
+    o = torch.full(q.shape, float("nan"), dtype=tdt, device="cuda")
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
     o, lse = fa_mod().attention(q, k, v, scale=scale, causal=causal, window=window,
-                                head_window=head_window, softcap=softcap)
+                                head_window=head_window, softcap=softcap, out=o, lse=lse)
     torch.cuda.synchronize()
     return host(o), host(lse)
 
@@ -254,8 +257,15 @@ def test_full_size_prefill_sampled(name):
 # -------------------------------------------------------------- split-KV
 def run_split(inp, S, scale, causal=False, window=0, softcap=0.0, out_dtype=None):
     q, k, v = (dev(inp[n], torch.bfloat16) for n in "qkv")
+    B, H, Nq, d = q.shape
+    # Partials start as NaN: every split of every row must be written
+    # (an empty split as m = -inf, l = 0, O = 0).
+    nan = float("nan")
+    parts = (torch.full((B, H, Nq, S, d), nan, device="cuda"), torch.full((B, H, Nq, S), nan, device="cuda"),
+             torch.full((B, H, Nq, S), nan, device="cuda"))
     o, lse, parts = fa_mod().splitkv_attention(q, k, v, S, scale=scale, causal=causal, window=window,
-                                               softcap=softcap, out_dtype=out_dtype, return_partials=True)
+                                               softcap=softcap, out_dtype=out_dtype, partials=parts,
+                                               return_partials=True)
     torch.cuda.synchronize()
     return host(o), host(lse), tuple(host(t) for t in parts)
 
