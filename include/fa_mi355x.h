@@ -66,7 +66,8 @@ typedef enum {
 typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
 
 /* Head sizes with kernels: d in {32, 64, 128}.  Per head, Nq*d and Nk*d
- * must be below 2^31 (FA_ERR_UNSUPPORTED otherwise). */
+ * must be below 2^31, and so must B*H and the grid's workgroup count
+ * (FA_ERR_UNSUPPORTED otherwise). */
 #define FA_MAX_HEAD_WINDOWS 256 /* largest H accepted with per-head windows */
 
 /*
@@ -86,7 +87,7 @@ typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
  * Errors: FA_ERR_INVALID_ARG for negative sizes, Hkv < 1, H % Hkv != 0, a
  * NULL q/k/v/o when the tensor is non-empty, window < 0, window > 0 without
  * causal, softcap < 0 or non-finite, non-finite scale; FA_ERR_UNSUPPORTED
- * for d not in {32, 64, 128} or Nq*d, Nk*d >= 2^31.
+ * for d not in {32, 64, 128} or Nq*d, Nk*d or B*H >= 2^31.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
@@ -219,7 +220,7 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part,
  * later one is written.  Asynchronous on stream.
  * Errors: FA_ERR_INVALID_ARG for negative sizes, pos < 0, window < 1,
  * sinks < 0, NULL pointers when B*Hkv*T*d > 0; FA_ERR_UNSUPPORTED for d not
- * in {32, 64, 128}.
+ * in {32, 64, 128} or B*Hkv*T >= 2^31.
  */
 int fa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                  int64_t B, int64_t Hkv, int64_t T, int64_t d,

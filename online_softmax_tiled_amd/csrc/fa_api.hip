@@ -13,6 +13,13 @@ using fa::FwdParams;
 
 bool supported_d(int64_t d) { return d == 32 || d == 64 || d == 128; }
 
+// a * b for non-negative sizes, saturated at INT64_MAX: a product of
+// absurd caller sizes then fails the limits below instead of wrapping.
+int64_t mul(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 // Checks shared by every forward entry point.  Fills p on success.
 int validate_fwd(const fa_fwd_args &a, FwdParams &p) {
     if (a.B < 0 || a.H < 0 || a.Hkv < 1 || a.Nq < 0 || a.Nk < 0 || a.d < 0) return FA_ERR_INVALID_ARG;
@@ -29,13 +36,15 @@ int validate_fwd(const fa_fwd_args &a, FwdParams &p) {
             if (a.head_window[h] > 0 && !a.causal) return FA_ERR_INVALID_ARG;
         }
     }
-    const bool q_nonempty = a.B * a.H * a.Nq * a.d > 0;
-    const bool kv_nonempty = a.B * a.Hkv * a.Nk * a.d > 0;
+    const bool q_nonempty = mul(mul(mul(a.B, a.H), a.Nq), a.d) > 0;
+    const bool kv_nonempty = mul(mul(mul(a.B, a.Hkv), a.Nk), a.d) > 0;
     if (q_nonempty && (!a.q || !a.o)) return FA_ERR_INVALID_ARG;
     if (kv_nonempty && (!a.k || !a.v)) return FA_ERR_INVALID_ARG;
     if (!supported_d(a.d)) return FA_ERR_UNSUPPORTED;
     // Per-head element offsets are 32-bit inside the kernels.
-    if (a.Nq * a.d > 0x7fffffff || a.Nk * a.d > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    if (mul(a.Nq, a.d) > 0x7fffffff || mul(a.Nk, a.d) > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+    // Query and K/V head counts over the batch are 32-bit inside the kernels.
+    if (mul(a.B, a.H) > 0x7fffffff) return FA_ERR_UNSUPPORTED;
 
     memset(&p, 0, sizeof p);
     p.q = a.q;
@@ -182,14 +191,15 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o_part, f
     FwdParams p;
     const int rc = validate_fwd(a, p);
     if (rc != FA_OK) return rc;
-    if (B * H * Nq > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
+    if (mul(mul(B, H), Nq) > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
     return run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
 }
 
 int fa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache, int64_t B, int64_t Hkv,
                  int64_t T, int64_t d, int64_t pos, int64_t window, int64_t sinks, fa_stream_t stream) {
     if (B < 0 || Hkv < 0 || T < 0 || d < 0 || !valid_rolling(pos, window, sinks)) return FA_ERR_INVALID_ARG;
-    const int64_t n_rows = B * Hkv * T;
+    const int64_t n_rows = mul(mul(B, Hkv), T);
+    if (n_rows > 0x7fffffff) return FA_ERR_UNSUPPORTED;
     if (n_rows > 0 && d > 0 && (!k_new || !v_new || !k_cache || !v_cache)) return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     return fa::launch_kv_append(k_new, v_new, k_cache, v_cache, n_rows, T, pos, window, sinks, (int)d,
@@ -210,7 +220,7 @@ int fa_decode_rolling(const void *q, const void *k_cache, const void *v_cache, f
     const int rc = validate_fwd(a, p);
     if (rc != FA_OK) return rc;
     if (rows * d > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    if (B * H > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
+    if (mul(B, H) > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
     p.kv_rows = rows;
     return run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
 }
@@ -219,7 +229,7 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part, vo
                int64_t H, int64_t Nq, int64_t d, int num_splits, int out_dtype, fa_stream_t stream) {
     if (B < 0 || H < 0 || Nq < 0 || d < 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
     if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
-    const int64_t rows = B * H * Nq;
+    const int64_t rows = mul(mul(B, H), Nq);
     if (rows > 0 && d > 0 && (!o_part || !m_part || !l_part || !o)) return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if (rows == 0) return FA_OK;

@@ -82,6 +82,11 @@ def call_fwd(**over):
     (dict(o=None), fa.FA_ERR_INVALID_ARG),
     (dict(d=48), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    # sizes whose products do not fit 64 bits are refused, not wrapped
+    (dict(Nq=1 << 62), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nk=1 << 62), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 40, Nq=1 << 40, Nk=1 << 20), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 30, H=8, Hkv=2), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_validation(over, status):
     assert call_fwd(**over) == status
@@ -143,6 +148,8 @@ def test_rolling_cache_validation():
     assert lib.fa_kv_append(*a3, 5, 8, 4, FAKE) == fa.FA_ERR_UNSUPPORTED        # d = 80
     a4 = list(app); a4[6] = 0; a4[0] = a4[1] = a4[2] = a4[3] = None
     assert lib.fa_kv_append(*a4, 5, 8, 4, FAKE) == fa.FA_OK                     # no tokens: no-op
+    a5 = list(app); a5[4] = a5[5] = a5[6] = 1 << 30
+    assert lib.fa_kv_append(*a5, 5, 8, 4, FAKE) == fa.FA_ERR_UNSUPPORTED        # B*Hkv*T beyond 2^63
     dec = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64]  # q, caches, partials, B, H, Hkv, d
     assert lib.fa_decode_rolling(*dec, 10, 8, 4, 0.1, 0.0, 0, FAKE) == fa.FA_ERR_INVALID_ARG   # num_splits
     assert lib.fa_decode_rolling(*dec, -2, 8, 4, 0.1, 0.0, 4, FAKE) == fa.FA_ERR_INVALID_ARG   # pos
