@@ -338,9 +338,10 @@ def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
         value, unit = wl.algorithmic_bytes(w) * len(rows) / total / secs / 1e9, "GB/s"
     else:
         value, unit = flops / secs / 1e12, "TFLOP/s"
+    what = (f"all {total} query rows" if stride == 1 else
+            f"one query row in {stride} ({len(rows)} of {total})")
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"every {stride}th query row of {w.name} ({len(rows)} of {total} rows, "
-                      f"{flops / 1e9:.1f} GFLOP fp64 in {secs:.1f} s)"}
+            "sample": f"{what} of {w.name} ({flops / 1e9:.1f} GFLOP fp64 in {secs:.1f} s)"}
 
 
 # rocprofv3 runs whose output --summarize-profiles reads (DIR = their -d root).
