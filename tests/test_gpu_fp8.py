@@ -213,6 +213,13 @@ SHAPES = [  # B, H, Hkv, Nq, Nk, d, causal, window
 ]
 
 
+def test_fp8_causal_block_order_clusters():
+    # B*Hkv = 40: each XCD takes 5 K/V heads of 16 blocks (8 query heads,
+    # 2 query tiles) in clusters of 4 + 1; every row must be written once.
+    print("case fp8 block order (5, 64, 8, 400, 400, 64)", flush=True)
+    check(narrow_inputs(5, 64, 8, 400, 400, 64, seed=21), 0.125, True, 0, "fp8 block order clusters")
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 def test_fp8_exact_weights(shape):
     B, H, Hkv, Nq, Nk, d, causal, window = shape

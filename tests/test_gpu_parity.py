@@ -167,6 +167,17 @@ def test_bf16_shapes(d, mode):
     parity(inp, "bf16", 1.0 / math.sqrt(d), what=f"bf16 {mode} d={d}", **kw)
 
 
+@pytest.mark.parametrize("shape", [(5, 32, 8, 1024, 64, 0), (5, 32, 8, 1024, 128, 300), (7, 8, 8, 4096, 32, 0)])
+def test_bf16_causal_block_order_clusters(shape):
+    # Causal grids whose B*Hkv is a multiple of 8 take their K/V heads in
+    # clusters per XCD; these shapes give clusters of 4 + 1 and 4 + 3 heads
+    # per XCD (a short last cluster).  Every row must be written once.
+    B, H, Hkv, N, d, W = shape
+    print(f"case bf16 block order {shape}", flush=True)
+    inp = rand_inputs(B, H, Hkv, N, N, d, seed=B * N + d, dtype="bf16")
+    parity(inp, "bf16", 1.0 / math.sqrt(d), causal=True, window=W, what=f"bf16 block order {shape}")
+
+
 def test_bf16_large_scores_stay_finite():
     # Scores scaled by 40: without the running maximum they overflow.
     inp = rand_inputs(1, 2, 2, 200, 260, 64, seed=5, dtype="bf16")
