@@ -40,8 +40,10 @@
 //     (bits 2 and 3 of the key index swapped), so the 8 keys a lane supplies
 //     to one P.V k-step are contiguous and the V^T operand is a single
 //     ds_read_b128 (the transposing read is several times slower per byte).
-//   * blocks are ordered so that all query tiles of one K/V head run back to
-//     back on the same XCD (shared L2), the longest causal tiles first.
+//   * all query tiles of one K/V head run on the same XCD (shared L2); a
+//     causal grid takes an XCD's heads a few at a time, longest query tile
+//     first across those heads (balanced tail, K and V of few heads live in
+//     the L2 at once).
 //
 // Softmax bookkeeping per tile is kept small, since at d = 128 its vector
 // work rivals the matrix work:
