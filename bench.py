@@ -611,9 +611,12 @@ Kernel trace statistics (`run_kernel_stats.csv`; warm-up included):
 
 {detail}
 
-A row (1 MB) is larger than on-chip memory and x (524 MB) larger than the
-256 MB Infinity Cache, so the softmax's second read comes from HBM again:
-its HBM read bytes are twice x.
+The softmax's read bytes are about twice x: FETCH_SIZE counts every read
+that misses the L2, whether the Infinity Cache (256 MB, memory side) or HBM
+serves it.  x (524 MB) exceeds that cache, but the second read walks each
+row backwards and finds the part read last in pass 1 still cached; the
+counters cannot show this, the kernel time does (284 us with a forward
+second read and non-temporal first read, 245 us now).
 """
     with open(os.path.join(ROOT, "profiles", "softmax_fp32_rows512_n256000.md"), "w") as f:
         f.write(md)
