@@ -9,6 +9,9 @@ Also: token streams through a rolling KV cache (random window, sinks, chunk
 sizes and check positions) and row softmax / fused top-k over random row
 lengths, both with the tolerances of their own test files.
 
+Also: causal bf16 grids with B*Hkv a multiple of 8 and several K/V heads
+per XCD, which the block order takes in clusters.
+
 FA_RANDOM_SHAPES_SCALE=k multiplies the number of seeds of every family (a
 longer sweep: k = 125 runs 1500 bf16, 1500 fp8, 1750 split-KV and 750 fp32
 cases in a few minutes on one MI355X)."""
@@ -61,6 +64,24 @@ def test_bf16_random_shapes(seed):
     print("case", what, flush=True)
     inp = tp.rand_inputs(B, H, Hkv, Nq, Nk, d, seed=seed, dtype="bf16")
     tp.parity(inp, "bf16", 1.0 / math.sqrt(d), causal=causal, window=window, softcap=softcap, what=what)
+
+
+@pytest.mark.parametrize("seed", range(6 * SCALE))
+def test_bf16_random_causal_head_clusters(seed):
+    # B*Hkv a multiple of 8 with several K/V heads per XCD: the causal block
+    # order takes them in clusters (and a short last cluster); both the
+    # 8-wave and the 4-wave grids occur.
+    rng = np.random.default_rng(7000 + seed)
+    Hkv = 8
+    H = Hkv * int(rng.choice([1, 2]))
+    B = int(rng.integers(3, 7))
+    N = int(rng.integers(200, 1100))
+    d = int(rng.choice([32, 64]))
+    window = int(rng.integers(1, 400)) if rng.random() < 0.3 else 0
+    what = f"bf16 clusters seed={seed} B={B} H={H} Hkv={Hkv} N={N} d={d} W={window}"
+    print("case", what, flush=True)
+    inp = tp.rand_inputs(B, H, Hkv, N, N, d, seed=seed, dtype="bf16")
+    tp.parity(inp, "bf16", 1.0 / math.sqrt(d), causal=True, window=window, what=what)
 
 
 @pytest.mark.parametrize("seed", range(6 * SCALE))
