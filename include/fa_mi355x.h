@@ -18,6 +18,13 @@
  * Pointers: device pointers (HBM), caller-allocated and caller-owned.  The
  *   library never allocates, frees or synchronises, keeps no state between
  *   calls and is safe to call from several host threads.
+ * Alignment: every tensor base pointer must be a multiple of 16 bytes (the
+ *   kernels move 16 bytes per lane to and from q, k, v, o, o_part and the
+ *   caches), except the fp32 row arrays lse, m_part and l_part (4 bytes) and
+ *   the arguments of fa_combine (natural alignment of their element type).
+ *   A misaligned pointer returns FA_ERR_INVALID_ARG.  Allocations from
+ *   hipMalloc (and torch) are aligned; a view that starts at an element
+ *   offset may not be.
  * Layouts: row-major, contiguous, no padding:
  *   q, o       [B, H,   Nq, d]
  *   k, v       [B, Hkv, Nk, d]
@@ -84,6 +91,13 @@ typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
  * the normaliser, and so lse, sums the fp32 weights.  (With a soft-cap up to
  * 60 the reference maximum stays 0; O is then divided by the sum of the
  * bf16 weights P.V used, lse still takes the fp32 sum.)
+ * Range with 0 < softcap <= 60: every weight is then e^z with |z| <= softcap
+ * instead of at most 1, so the fp32 output accumulator of a row reaches up
+ * to e^softcap * sum_j |v_j| over its visible keys.  That sum must stay
+ * below the fp32 maximum (3.4e38), i.e. max|v| * Nk < 3.4e38 / e^softcap:
+ * at 16384 keys, |v| below about 4e12 for softcap 50 and 1.8e8 for softcap
+ * 60.  Beyond that the result overflows to inf/NaN; a softcap above 60 takes
+ * the running maximum, whose weights never exceed 1.
  * Errors: FA_ERR_INVALID_ARG for negative sizes, Hkv < 1, H % Hkv != 0, a
  * NULL q/k/v/o when the tensor is non-empty, window < 0, window > 0 without
  * causal, softcap < 0 or non-finite, non-finite scale; FA_ERR_UNSUPPORTED
@@ -107,8 +121,9 @@ int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *
  * section 16.3, alternating local and global attention).
  *
  * dtype selects bf16 (FA_DTYPE_BF16) or fp32 (FA_DTYPE_FP32) tensors.
- * head_window: NULL (every head uses `window`) or a HOST array of H int32
- * values, each 0 (no window) or > 0; read during the call only.  H may be at
+ * head_window: NULL (every head uses `window`) or a HOST array of exactly H
+ * int32 values (entry h for query head h; the library reads all H of them),
+ * each 0 (no window) or > 0; read during the call only.  H may be at
  * most FA_MAX_HEAD_WINDOWS when head_window is given (else
  * FA_ERR_UNSUPPORTED).  A positive entry needs causal.
  */

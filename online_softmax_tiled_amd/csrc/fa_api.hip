@@ -13,6 +13,12 @@ using fa::FwdParams;
 
 bool supported_d(int64_t d) { return d == 32 || d == 64 || d == 128; }
 
+// The kernels move 16 bytes per lane from and to the tensor base pointers
+// (vector loads, direct-to-LDS buffer loads, vector stores), and 4 bytes
+// for the fp32 row arrays; a misaligned base pointer (say a view with an
+// odd element offset) is refused instead of faulting or being rounded down.
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
 // a * b for non-negative sizes, saturated at INT64_MAX: a product of
 // absurd caller sizes then fails the limits below instead of wrapping.
 int64_t mul(int64_t a, int64_t b) {
@@ -40,6 +46,8 @@ int validate_fwd(const fa_fwd_args &a, FwdParams &p) {
     const bool kv_nonempty = mul(mul(mul(a.B, a.Hkv), a.Nk), a.d) > 0;
     if (q_nonempty && (!a.q || !a.o)) return FA_ERR_INVALID_ARG;
     if (kv_nonempty && (!a.k || !a.v)) return FA_ERR_INVALID_ARG;
+    if (!aligned(a.q, 16) || !aligned(a.o, 16) || !aligned(a.k, 16) || !aligned(a.v, 16) || !aligned(a.lse, 4))
+        return FA_ERR_INVALID_ARG;
     if (!supported_d(a.d)) return FA_ERR_UNSUPPORTED;
     // Per-head element offsets are 32-bit inside the kernels.
     if (mul(a.Nq, a.d) > 0x7fffffff || mul(a.Nk, a.d) > 0x7fffffff) return FA_ERR_UNSUPPORTED;
@@ -192,6 +200,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, float *o_part, f
     const int rc = validate_fwd(a, p);
     if (rc != FA_OK) return rc;
     if (mul(mul(B, H), Nq) > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
+    if (!aligned(m_part, 4) || !aligned(l_part, 4)) return FA_ERR_INVALID_ARG;
     return run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
 }
 
@@ -201,6 +210,8 @@ int fa_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_ca
     const int64_t n_rows = mul(mul(B, Hkv), T);
     if (n_rows > 0x7fffffff) return FA_ERR_UNSUPPORTED;
     if (n_rows > 0 && d > 0 && (!k_new || !v_new || !k_cache || !v_cache)) return FA_ERR_INVALID_ARG;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     return fa::launch_kv_append(k_new, v_new, k_cache, v_cache, n_rows, T, pos, window, sinks, (int)d,
                                 reinterpret_cast<hipStream_t>(stream));
@@ -221,6 +232,7 @@ int fa_decode_rolling(const void *q, const void *k_cache, const void *v_cache, f
     if (rc != FA_OK) return rc;
     if (rows * d > 0x7fffffff) return FA_ERR_UNSUPPORTED;
     if (mul(B, H) > 0 && (!o_part || !m_part || !l_part)) return FA_ERR_INVALID_ARG;
+    if (!aligned(m_part, 4) || !aligned(l_part, 4)) return FA_ERR_INVALID_ARG;
     p.kv_rows = rows;
     return run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
 }
@@ -231,6 +243,9 @@ int fa_combine(const float *o_part, const float *m_part, const float *l_part, vo
     if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
     const int64_t rows = mul(mul(B, H), Nq);
     if (rows > 0 && d > 0 && (!o_part || !m_part || !l_part || !o)) return FA_ERR_INVALID_ARG;
+    if (!aligned(o_part, 4) || !aligned(m_part, 4) || !aligned(l_part, 4) || !aligned(lse, 4) ||
+        !aligned(o, out_dtype == FA_DTYPE_BF16 ? 2 : 4))
+        return FA_ERR_INVALID_ARG;
     if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
     if (rows == 0) return FA_OK;
     return fa::launch_combine(o_part, m_part, l_part, o, lse, rows, num_splits, (int)d, out_dtype,

@@ -139,6 +139,9 @@ def fa_fwd_ex(dtype, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, windo
               head_window=None, stream=None):
     hw = None
     if head_window is not None:
+        # The library reads head_window[h] for every h < H.
+        if len(head_window) != int(H):
+            raise ValueError(f"head_window has {len(head_window)} entries; it needs one per query head (H={H})")
         hw = (ctypes.c_int32 * len(head_window))(*[int(x) for x in head_window])
     a = FwdArgs(int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d,
                 float(scale), int(causal), int(window), float(softcap),
@@ -204,12 +207,21 @@ def _shapes(q, k, v):
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
+        _check_aligned(t, 16, "q, k, v")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
     return B, H, Hkv, Nq, Nk, d
 
 
-def _buffer(t, shape, dtype, device, name):
+def _check_aligned(t, nbytes, name):
+    """The kernels move 16 bytes per lane from and to the base of q, k, v, o
+    and the partials (4 bytes for fp32 row arrays); a view that starts at an
+    element offset may break that, and the library would refuse it."""
+    if t.numel() and t.data_ptr() % nbytes:
+        raise ValueError(f"{name} must start at a {nbytes}-byte aligned address (got a view at an offset)")
+
+
+def _buffer(t, shape, dtype, device, name, align=16):
     """A caller-supplied output buffer: it must be a contiguous device tensor
     of exactly this shape and dtype (the kernels write every element of it
     and nothing past it)."""
@@ -220,6 +232,7 @@ def _buffer(t, shape, dtype, device, name):
     if tuple(t.shape) != shape or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {dtype} device tensor of shape {list(shape)}, "
                          f"got {t.dtype} {list(t.shape)}")
+    _check_aligned(t, align, name)
     return t
 
 
@@ -237,7 +250,7 @@ def attention(q, k, v, scale=None, causal=False, window=0, head_window=None, sof
     else:
         raise ValueError("q, k, v must be bfloat16 or float32")
     o = _buffer(out, q.shape, q.dtype, q.device, "out")
-    lse = _buffer(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    lse = _buffer(lse, (B, H, Nq), torch.float32, q.device, "lse", align=4)
     if head_window is not None:
         fa_fwd_ex(dtype, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap,
                   head_window=head_window)
@@ -259,7 +272,7 @@ def attention_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, scale=No
     B, H, Hkv, Nq, Nk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     o = _buffer(out, (B, H, Nq, d), torch.bfloat16, q.device, "out")
-    lse = _buffer(lse, (B, H, Nq), torch.float32, q.device, "lse")
+    lse = _buffer(lse, (B, H, Nq), torch.float32, q.device, "lse", align=4)
     fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale, causal, window)
     return o, lse
 
@@ -277,8 +290,8 @@ def splitkv_attention(q, k, v, num_splits, scale=None, causal=False, window=0, s
     S = int(num_splits)
     o_part, m_part, l_part = (None, None, None) if partials is None else partials
     o_part = _buffer(o_part, (B, H, Nq, S, d), torch.float32, q.device, "o_part")
-    m_part = _buffer(m_part, (B, H, Nq, S), torch.float32, q.device, "m_part")
-    l_part = _buffer(l_part, (B, H, Nq, S), torch.float32, q.device, "l_part")
+    m_part = _buffer(m_part, (B, H, Nq, S), torch.float32, q.device, "m_part", align=4)
+    l_part = _buffer(l_part, (B, H, Nq, S), torch.float32, q.device, "l_part", align=4)
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     o = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)

@@ -227,3 +227,40 @@ def test_binding_rejects_mis_sized_output_buffers():
                 torch.empty(2, 3)):
         with pytest.raises(ValueError, match="out must be"):
             fa._buffer(bad, (2, 3), torch.float32, "cpu", "out")
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_misaligned_tensor_pointers_are_refused(which):
+    # Every kernel moves 16 bytes per lane from the tensor base pointers: an
+    # address off by one bf16 element is refused before any launch.
+    assert call_fwd(**{which: FAKE + 2}) == fa.FA_ERR_INVALID_ARG
+    assert call_fwd(**{which: FAKE + 8}) == fa.FA_ERR_INVALID_ARG
+    assert call_fp8(**{which: FAKE + 4}) == fa.FA_ERR_INVALID_ARG
+
+
+def test_misaligned_row_arrays_and_partials_are_refused():
+    lib = fa.load_library()
+    assert call_fwd(lse=FAKE + 2) == fa.FA_ERR_INVALID_ARG
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 1, 64, 64, 0.1, 0, 0, 0.0]
+    for i, off in ((3, 4), (4, 2), (5, 1)):              # o_part (16-byte), m_part, l_part (4-byte)
+        b = list(base); b[i] = FAKE + off
+        assert lib.fa_fwd_splitkv(*b, 4, FAKE) == fa.FA_ERR_INVALID_ARG
+    c = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 1, 64]
+    assert lib.fa_combine(*c[:3], FAKE + 1, *c[4:], 4, fa.FA_DTYPE_BF16, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_combine(*c[:3], FAKE + 2, *c[4:], 4, fa.FA_DTYPE_FP32, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_combine(FAKE + 2, *c[1:], 4, fa.FA_DTYPE_FP32, FAKE) == fa.FA_ERR_INVALID_ARG
+    app = [FAKE, FAKE, FAKE + 8, FAKE, 2, 2, 3, 64]
+    assert lib.fa_kv_append(*app, 5, 8, 4, FAKE) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_checks_head_window_length_and_alignment():
+    # The library reads head_window[h] for all H heads: a shorter list is
+    # refused by the binding before the call.
+    with pytest.raises(ValueError, match="one per query head"):
+        fa.fa_fwd_ex(fa.FA_DTYPE_BF16, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 8, 8, 64, 0.1, 1, 0, 0.0,
+                     head_window=[0, 16, 0])
+    torch = pytest.importorskip("torch")
+    x = torch.empty(40, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="aligned"):
+        fa._check_aligned(x[1:], 16, "q")
+    fa._check_aligned(x[8:], 16, "q")

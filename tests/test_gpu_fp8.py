@@ -289,25 +289,13 @@ def test_fp8_bad_arguments():
         fa.fa_fwd_fp8(q, q, q, o, None, 1, 1, 1, 4, 4, 128, 0.1, 1.0, 1.0, 1.0, 0, 5)  # window w/o causal
 
 
-def test_fp8_full_size_prefill_sampled():
-    # the benchmark's launch: B=4, H=32, 4096 x 4096, d=128, causal; the
-    # oracle checks sampled rows of it (rows at the 256-row block edges and
-    # random rows)
+@pytest.mark.timeout(900)
+def test_fp8_full_size_prefill_all_rows():
+    # the benchmark's launch: B=4, H=32, 4096 x 4096, d=128, causal; every
+    # row against the oracle and the bounds above, over the whole output
     w = wl.FP8_PREFILL
-    print(f"case fp8 full size {w.name}", flush=True)
+    print(f"case fp8 full size {w.name} (all rows)", flush=True)
     x = wl.generate_fp8(w)
-    o, lse = run(x, w.scale, w.causal, w.window)
-    # Every row sees at least its own key: all of O and lse is written.
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    rng = np.random.default_rng(0)
-    Nq = w.Nq
-    picks = {0, 1, 255, 256, 257, Nq - 1, Nq - 2, Nq - 256, 4 * Nq + 4095, (w.B * w.H - 1) * Nq + 1000}
-    picks.update(rng.integers(0, w.B * w.H * Nq, size=200).tolist())
-    rows = np.array(sorted(picks), dtype=np.int64)
-    ref = oracle_fp8(x, w.scale, w.causal, w.window, rows=rows)
-    rig, mean_elem, lse_b = bounds(x, w.scale, w.causal, w.window, ref, rows=rows)
-    got = o.reshape(-1, w.d)[rows]
-    err = np.abs(got - ref["o"])
-    assert np.all(err <= rig), f"worst excess {np.max(err - rig):.3g}"
-    assert err.mean() <= mean_elem.mean() + 1e-7
-    assert np.all(np.abs(lse.reshape(-1)[rows] - ref["lse"]) <= lse_b)
+    mean_err, mean_bound = check(x, w.scale, w.causal, w.window, w.name)
+    print(f"{w.name}: all {w.B * w.H * w.Nq} rows within the per-element bounds; mean |dO| {mean_err:.3e} "
+          f"(bound {mean_bound:.3e})", flush=True)

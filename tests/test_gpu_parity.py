@@ -7,8 +7,8 @@ the same bf16/fp32 values go to both sides.  Tolerances:
     |lse| error <= 1e-4 * max(1, |lse|) (every bf16 path sums the fp32 weights
     into the normaliser, so lse carries no bf16 rounding; the partial sums
     are held to the same relative bound).
-Full-size workloads are checked on sampled rows the oracle computes one by
-one, in the launch configuration the benchmark times.
+Full-size workloads are checked on every row, in the launch configuration
+the benchmark times.
 """
 import math
 
@@ -227,42 +227,27 @@ def test_single_key_and_uniform_scores():
     assert np.max(np.abs(o[0] - mean)) < 2e-2
 
 
-# ------------------------------------------------------- full-size, sampled
-def sample_rows(w, rng, n_random=256):
-    """Rows (flat indices) spanning heads, tile edges and window edges."""
-    Nq = w.Nq
-    picks = set()
-    for b in {0, w.B - 1}:
-        for h in sorted({0, 1, w.H // 2, w.H - 1}):
-            base = (b * w.H + h) * Nq
-            for i in [0, 1, 63, 64, 127, 128, 129, Nq // 2, Nq - 129, Nq - 2, Nq - 1]:
-                if 0 <= i < Nq:
-                    picks.add(base + i)
-            W = int(w.windows()[h])
-            if W > 0:
-                for i in (W - 2, W - 1, W, W + 1, W + 127, W + 128):
-                    if 0 <= i < Nq:
-                        picks.add(base + i)
-    picks.update(rng.integers(0, w.B * w.H * Nq, size=n_random).tolist())
-    return np.array(sorted(picks), dtype=np.int64)
-
-
+# ------------------------------------------------------- full-size, all rows
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["bf16_causal_b4_h32_n4096_d128", "bf16_gqa_swa_softcap_h32kv8_n16384_d128"])
-def test_full_size_prefill_sampled(name):
+def test_full_size_prefill_all_rows(name):
+    # The benchmark's launch at full size, every one of the B*H*Nq rows
+    # compared with the oracle (threaded over the host cores), and the
+    # max-abs / mean-abs / lse criteria evaluated over the whole output.
     w = wl.WORKLOADS[name]
-    print(f"case {name} (full size, sampled rows)", flush=True)
+    print(f"case {name} (full size, all rows)", flush=True)
     inp = wl.generate(w)
     hw = list(w.head_window) if w.head_window else None
     o, lse = run_gpu(inp, "bf16", w.scale, causal=w.causal, window=w.window, head_window=hw,
                      softcap=w.softcap)
-    rows = sample_rows(w, np.random.default_rng(1))
     ref = oracle.attention(inp["q"], inp["k"], inp["v"], w.scale, causal=w.causal, window=w.window,
-                           head_window=hw, softcap=w.softcap, rows=rows)
-    check_o(o.reshape(-1, w.d)[rows], ref["o"], "bf16", name)
-    check_lse(lse.reshape(-1)[rows], ref["lse"], "bf16", name)
-    # every row is finite; every row's output is a convex combination of V
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    assert np.max(np.abs(o)) <= np.max(np.abs(inp["v"])) + 1e-2
+                           head_window=hw, softcap=w.softcap)
+    err = np.abs(o - ref["o"])
+    lerr = np.abs(lse - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))
+    print(f"{name}: all {o.shape[0] * o.shape[1] * o.shape[2]} rows: max |dO| {err.max():.3e}, "
+          f"mean |dO| {err.mean():.3e}, max lse rel err {lerr.max():.3e}", flush=True)
+    check_o(o, ref["o"], "bf16", name)
+    check_lse(lse, ref["lse"], "bf16", name)
 
 
 # -------------------------------------------------------------- split-KV
