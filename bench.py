@@ -50,6 +50,10 @@ from online_softmax_tiled_amd import workloads as wl  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Untimed wall time each leg runs before its counted warm-up launches: an
+# idle MI355X takes tens of milliseconds to reach its working clocks, and a
+# few warm-up launches of a sub-millisecond kernel do not cover that.
+SETTLE_MS = 200.0
 METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak); decode GB/s (% HBM peak)"
 PREFILL = "bf16_causal_b4_h32_n4096_d128"
 DECODE = "bf16_splitkv_decode_b16_h32kv8_nk32768_d128"
@@ -87,89 +91,111 @@ def measured_traffic(kind: str):
     return rec.get("bytes_per_launch")
 
 
-def to_device(inp, torch):
-    return {n: torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv"}
-
-
-def time_launches(launch, steps, warmup, torch):
-    """Warmup, then `steps` back-to-back launches bracketed by one pair of
-    HIP events on the launch stream (no events between launches).  Returns
-    (average ms per launch, total ms, wall seconds)."""
-    for _ in range(warmup):
-        launch()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
-        launch()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total = start.elapsed_time(end)
-    return total / steps, total, wall
-
-
-def bench_prefill(torch, fa, steps, warmup):
-    w = wl.WORKLOADS[PREFILL]
-    t = to_device(wl.generate(w), torch)
-    o = torch.empty_like(t["q"])
-    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
-    args = (t["q"], t["k"], t["v"], o, lse, w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, w.scale, int(w.causal),
-            w.window, w.softcap)
-
-    def launch():
-        fa.fa_fwd(*args)
-
-    avg, total, wall = time_launches(launch, steps, warmup, torch)
-    flops = wl.algorithmic_flops(w)
-    achieved = flops / (avg * 1e-3) / 1e12
-    traffic = measured_traffic("prefill")
-    return w, {
-        "flops": flops, "avg_ms": avg, "total_ms": total, "wall_s": wall,
-        "value": flops * steps / (total * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
-    }
-
-
 # Other prefill configurations reported beside the headline one (TFLOP/s and
 # fraction of the bf16 peak): non-causal small heads, and causal GQA with
 # sliding windows on even heads and a soft-cap (the fixed-maximum kernel).
 OTHER_PREFILL = ("bf16_b1_h8_n1024_d64", "bf16_gqa_swa_softcap_h32kv8_n16384_d128")
 
 
-def bench_prefill_config(torch, fa, name, steps, warmup):
+def to_device(inp, torch):
+    return {n: torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv"}
+
+
+class Timing:
+    """Event timings of one leg: `total_ms` between one event pair around
+    all K steps, and per step (and per kernel of a step) the time between
+    events recorded before and after it on the launch stream."""
+
+    def __init__(self, total_ms, wall_s, step_ms, part_ms):
+        self.total_ms, self.wall_s = total_ms, wall_s
+        self.step_ms, self.part_ms = step_ms, part_ms
+
+    @staticmethod
+    def stats(ms):
+        a = np.asarray(ms, dtype=np.float64)
+        return {"mean_ms": round(float(a.mean()), 5), "median_ms": round(float(np.median(a)), 5),
+                "min_ms": round(float(a.min()), 5), "max_ms": round(float(a.max()), 5)}
+
+    def per_step(self, steps):
+        return self.total_ms / steps
+
+
+def time_leg(parts, steps, warmup, settle_ms, torch):
+    """One leg: a step launches every callable in `parts` in order.  Runs
+    untimed launches for `settle_ms` of wall time (the GPU leaves its idle
+    clock state; 0 skips this) and `warmup` untimed steps; then the timed
+    region: exactly `steps` steps back to back between one pair of events
+    (total_ms: value and ms_per_step).  A second pass of `steps` steps then
+    records events before and after every kernel of every step, for the
+    per-launch durations (mean, median, minimum) of each kernel; those
+    events would add their own few microseconds to the first pass.  All
+    events are recorded on the launch stream."""
+    def step():
+        for p in parts:
+            p()
+    if settle_ms > 0:
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                step()
+            torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total = start.elapsed_time(end)
+    n = len(parts)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        for j, p in enumerate(parts):
+            p()
+            e[j + 1].record()
+    torch.cuda.synchronize()
+    step_ms = [e[0].elapsed_time(e[n]) for e in ev]
+    part_ms = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(n)]
+    return Timing(total, wall, step_ms, part_ms)
+
+
+# ---------------------------------------------------------------- the legs
+# Each prepare_* function generates the leg's seeded inputs, uploads them and
+# returns the callables of one step; every leg is prepared before any leg is
+# timed, so the GPU never waits for host-side input generation between legs.
+
+def prepare_prefill(torch, fa, name=PREFILL):
     w = wl.WORKLOADS[name]
     t = to_device(wl.generate(w), torch)
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
     hw = list(w.head_window) if w.head_window else None
-    # The argument block is built once (the smaller workload's launches take
+    # The argument block is built once (the smaller workloads' launches take
     # tens of microseconds; rebuilding it per launch would time the host).
     import ctypes
     from online_softmax_tiled_amd.fa import FwdArgs
     hw_arr = (ctypes.c_int32 * len(hw))(*hw) if hw else None
     a = FwdArgs(0, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), o.data_ptr(), lse.data_ptr(),
-                   w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, float(w.scale), int(w.causal), int(w.window),
-                   float(w.softcap), ctypes.cast(hw_arr, ctypes.POINTER(ctypes.c_int32)) if hw else None,
-                   torch.cuda.current_stream().cuda_stream or None)
+                w.B, w.H, w.Hkv, w.Nq, w.Nk, w.d, float(w.scale), int(w.causal), int(w.window),
+                float(w.softcap), ctypes.cast(hw_arr, ctypes.POINTER(ctypes.c_int32)) if hw else None,
+                torch.cuda.current_stream().cuda_stream or None)
     lib, ref = fa.load_library(), ctypes.byref(a)
+    keep = (t, o, lse, hw_arr, a)
 
     def launch():
         if lib.fa_fwd_ex(ref) != 0:
             raise RuntimeError("fa_fwd_ex failed")
-
-    avg, total, wall = time_launches(launch, steps, warmup, torch)
-    flops = wl.algorithmic_flops(w)
-    value = flops * steps / (total * 1e-3) / 1e12
-    return {"workload": name, "value": round(value, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(total / steps, 4), "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-            "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
-                       "head_window": "W on even heads" if hw else None, "softcap": w.softcap or None}}
+    launch.keep = keep
+    return w, [launch]
 
 
-def bench_prefill_fp8(torch, fa, steps, warmup):
+def prepare_prefill_fp8(torch, fa):
     w = wl.FP8_PREFILL
     x = wl.generate_fp8(w)
     t = {n: torch.from_numpy(x[n]).cuda() for n in "qkv"}
@@ -180,20 +206,10 @@ def bench_prefill_fp8(torch, fa, steps, warmup):
 
     def launch():
         fa.fa_fwd_fp8(*args)
-
-    avg, total, wall = time_launches(launch, steps, warmup, torch)
-    flops = wl.algorithmic_flops(w)
-    achieved = flops / (avg * 1e-3) / 1e12
-    return w, {
-        "flops": flops, "avg_ms": avg, "total_ms": total, "wall_s": wall,
-        "value": flops * steps / (total * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_fp8")},
-    }
+    return w, [launch]
 
 
-def bench_decode(torch, fa, steps, warmup):
+def prepare_decode(torch, fa):
     w = wl.WORKLOADS[DECODE]
     t = to_device(wl.generate(w), torch)
     S = w.num_splits
@@ -209,28 +225,10 @@ def bench_decode(torch, fa, steps, warmup):
 
     def combine():
         fa.fa_combine(o_part, m_part, l_part, o, lse, w.B, w.H, w.Nq, w.d, S, 0)
-
-    def launch():
-        split()
-        combine()
-
-    avg, total, wall = time_launches(launch, steps, warmup, torch)
-    # the split kernel alone (the dominant kernel) for the roofline
-    avg_split, _, _ = time_launches(split, steps, 2, torch)
-    nbytes = wl.algorithmic_bytes(w)
-    part_bytes = w.B * w.H * w.Nq * S * (w.d + 2) * 4
-    split_bytes = nbytes - part_bytes - (w.B * w.H * w.Nq * (w.d * 2 + 4))  # q, k, v in; partials out
-    achieved = split_bytes / (avg_split * 1e-3) / 1e9
-    return w, {
-        "bytes": nbytes, "avg_ms": avg, "total_ms": total, "wall_s": wall,
-        "value": nbytes * steps / (total * 1e-3) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode"),
-                     "kernel": "splitkv_decode_kernel", "avg_ms": round(avg_split, 4)},
-    }
+    return w, [split, combine]
 
 
-def bench_rolling(torch, fa, steps, warmup):
+def prepare_rolling(torch, fa):
     """Streaming decode over a rolling KV cache with attention sinks: a step
     appends one token's K/V (fa_kv_append) and runs fa_decode_rolling +
     fa_combine for its query, at a fixed position far into the stream."""
@@ -252,35 +250,22 @@ def bench_rolling(torch, fa, steps, warmup):
     o = torch.empty((w.B, w.H, 1, w.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.H, 1), dtype=torch.float32, device="cuda")
 
+    def append():
+        fa.fa_kv_append(kn, vn, kc, vc, w.B, w.Hkv, 1, w.d, w.pos, w.window, w.sinks)
+
     def decode():
         fa.fa_decode_rolling(q, kc, vc, o_part, m_part, l_part, w.B, w.H, w.Hkv, w.d, w.pos, w.window, w.sinks,
                              w.scale, 0.0, S)
 
-    def launch():
-        fa.fa_kv_append(kn, vn, kc, vc, w.B, w.Hkv, 1, w.d, w.pos, w.window, w.sinks)
-        decode()
+    def combine():
         fa.fa_combine(o_part, m_part, l_part, o, lse, w.B, w.H, 1, w.d, S, 0)
-
-    avg, total, wall = time_launches(launch, steps, warmup, torch)
-    avg_dec, _, _ = time_launches(decode, steps, 2, torch)
-    nbytes = wl.rolling_bytes(w)
-    dec_bytes = 2 * w.rows * w.B * w.Hkv * w.d * 2 + w.B * w.H * w.d * 2 + w.B * w.H * S * (w.d + 2) * 4
-    achieved = dec_bytes / (avg_dec * 1e-3) / 1e9
-    return {
-        "workload": w.name, "value": round(nbytes * steps / (total * 1e-3) / 1e9, 1), "unit": "GB/s",
-        "ms_per_step": round(total / steps, 4), "frac_of_hbm_peak": round(nbytes * steps / (total * 1e-3) / 1e9
-                                                                        / PEAK_HBM_GBS, 4),
-        "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "d": w.d, "window": w.window, "sinks": w.sinks,
-                   "pos": w.pos, "cache_rows_read": w.rows, "num_splits": S},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic("rolling_decode"),
-                     "kernel": "splitkv_decode_kernel (rolling cache)", "avg_ms": round(avg_dec, 4)},
-    }
+    return w, [append, decode, combine]
 
 
-def bench_softmax(torch, fa, steps, warmup):
+def prepare_softmax(torch, fa):
     """Row softmax with the online normaliser and the fused softmax top-k on
-    vocabulary-sized rows (fp32)."""
+    vocabulary-sized rows (fp32); torch's softmax and softmax + topk on the
+    same rows are timed beside them for context."""
     w = wl.SOFTMAX
     rng = np.random.default_rng(w.seed)
     x = torch.from_numpy((rng.standard_normal((w.rows, w.n)) * 3.0).astype(np.float32)).cuda()
@@ -294,16 +279,31 @@ def bench_softmax(torch, fa, steps, warmup):
     def tk():
         fa.fa_softmax_topk(x, probs, idx, None, w.rows, w.n, w.k, fa.fa.FA_DTYPE_FP32)
 
-    b = wl.softmax_bytes(w)
-    out = {"workload": w.name, "config": {"rows": w.rows, "n": w.n, "k": w.k, "dtype": "fp32"}}
-    for name, fn, nbytes in (("softmax", sm, b["softmax_online"]), ("topk", tk, b["topk_fused"])):
-        avg, total, _ = time_launches(fn, steps, warmup, torch)
-        gbs = nbytes / (avg * 1e-3) / 1e9
-        out[name] = {"ms_per_step": round(avg, 4), "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
-                     "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name)}
-    out["softmax"]["bytes_note"] = "two reads of x and one write of y (online normaliser)"
-    out["topk"]["bytes_note"] = "one read of x; k probabilities and indices written"
-    return out
+    def torch_sm():
+        torch.softmax(x, dim=-1)
+
+    def torch_tk():
+        torch.topk(torch.softmax(x, dim=-1), w.k, dim=-1)
+    return w, {"softmax": [sm], "topk": [tk], "torch_softmax": [torch_sm], "torch_softmax_topk": [torch_tk]}
+
+
+def prepare_standard_attention(torch):
+    """Standard attention with the score matrix materialised in HBM (two
+    torch bf16 matrix products and an fp32 softmax over the masked scores),
+    on the first batch element of the causal prefill workload: the baseline
+    that the pages' FlashAttention speedup figure compares against."""
+    w = wl.WORKLOADS[PREFILL].with_(B=1)
+    t = to_device(wl.generate(w), torch)
+    q, v = t["q"], t["v"]
+    kt = t["k"].transpose(-1, -2).contiguous()
+    mask = torch.ones((w.Nq, w.Nk), dtype=torch.bool, device="cuda").triu_(1)
+
+    def launch():
+        s = torch.matmul(q, kt).float().mul_(w.scale).masked_fill_(mask, float("-inf"))
+        p = torch.softmax(s, dim=-1).to(torch.bfloat16)
+        del s
+        torch.matmul(p, v)
+    return w, [launch]
 
 
 def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
@@ -341,7 +341,82 @@ def cpu_baseline(w, target_s: float = 15.0, max_threads: int = 16):
     what = (f"all {total} query rows" if stride == 1 else
             f"one query row in {stride} ({len(rows)} of {total})")
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{what} of {w.name} ({flops / 1e9:.1f} GFLOP fp64 in {secs:.1f} s)"}
+            "sample": f"{what} of {w.name} ({flops / 1e9:.1f} GFLOP fp64 in {secs:.1f} s)",
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_info(torch):
+    """The GPU's compute-unit count and maximum clock as rocminfo reports
+    them, the dense bf16 MFMA peak they imply (4 SIMDs per CU, each 1024
+    bf16 FLOP per clock on gfx950), and a measured device-to-device copy
+    rate as a check of the HBM figure."""
+    import subprocess
+    info = {"name": torch.cuda.get_device_name(0),
+            "torch_multiprocessor_count": torch.cuda.get_device_properties(0).multi_processor_count}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        agent = None
+        for blk in out.split("Agent ")[1:]:
+            if "gfx950" in blk and "Compute Unit:" in blk:
+                agent = blk
+                break
+        if agent is not None:
+            def field(key):
+                for line in agent.splitlines():
+                    if line.strip().startswith(key):
+                        return line.split(":", 1)[1].split()[0]
+                return None
+            cu, mhz = int(field("Compute Unit")), int(field("Max Clock Freq. (MHz)"))
+            info["rocminfo"] = {"compute_units": cu, "max_clock_mhz": mhz,
+                                "bf16_dense_peak_tflops": round(cu * 4 * 1024 * mhz * 1e6 / 1e12, 1),
+                                "fp8_dense_peak_tflops": round(cu * 4 * 2048 * mhz * 1e6 / 1e12, 1)}
+    except (OSError, subprocess.SubprocessError, ValueError, TypeError):
+        info["rocminfo"] = None
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    times = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    info["copy_1GiB"] = {"median_ms": round(float(np.median(times)), 4),
+                         "gbs_read_plus_write": round(2 * n / (float(np.median(times)) * 1e-3) / 1e9, 1)}
+    del src, dst
+    return info
+
+
+# The pages' own figures (context, not targets: none is an MI355X number).
+PAGES_CONTEXT = [
+    {"figure": "FlashAttention speedup over standard attention, often quoted as 3x to 5x",
+     "source": "Transformers & Math, Module 16, section 16.2 (hardware not stated)",
+     "measured_here": "standard_attention.speedup (same GPU, first batch element of the causal prefill workload)"},
+    {"figure": "online-normaliser softmax up to 1.3x faster than the safe softmax",
+     "source": "Online normalizer calculation for softmax, abstract (hardware not stated)",
+     "measured_here": "softmax.softmax.byte_ratio_vs_three_pass, softmax.softmax.speedup_vs_torch"},
+    {"figure": "softmax fused with top-k up to 5x faster",
+     "source": "Online normalizer calculation for softmax, abstract (hardware not stated)",
+     "measured_here": "softmax.topk.byte_ratio_vs_unfused, softmax.topk.speedup_vs_torch"},
+    {"figure": "block-wise CPU attention 2-5x faster, about 75% less memory",
+     "source": "oxios_kernel flash_attention.rs, module documentation (single-thread CPU, f32)",
+     "measured_here": "cpu_baseline (the oracle is the direct definition, not a blocked CPU kernel)"},
+]
 
 
 # rocprofv3 runs whose output --summarize-profiles reads (DIR = their -d root).
@@ -627,12 +702,14 @@ second read and non-temporal first read, 245 us now).
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed launches of each leg for this much wall time before its warm-up")
     ap.add_argument("--workload", choices=["prefill", "decode", "prefill_fp8", "rolling", "softmax"],
                     default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="prefill leg only (no decode or rolling legs)")
+    ap.add_argument("--no-decode", action="store_true", help="prefill leg only (no other legs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM byte counters)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -658,72 +735,194 @@ def main():
     import online_softmax_tiled_amd as fa
     fa.load_library()
     torch.cuda.init()
+    K, W, settle = args.steps, args.warmup, args.settle_ms
 
-    if args.workload in ("rolling", "softmax"):
-        r = (bench_rolling if args.workload == "rolling" else bench_softmax)(torch, fa, args.steps, args.warmup)
-        print(json.dumps({"leg": args.workload, **r}), flush=True)
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---- every leg's inputs generated and uploaded before any timing
+    wk = args.workload
+    all_legs = wk == "prefill" and not args.no_decode
+    prep = {}
+    if wk == "prefill":
+        prep["prefill"] = prepare_prefill(torch, fa)
+    if wk == "decode" or all_legs:
+        prep["decode"] = prepare_decode(torch, fa)
+    if wk == "rolling" or all_legs:
+        prep["rolling"] = prepare_rolling(torch, fa)
+    if wk == "softmax" or all_legs:
+        prep["softmax"] = prepare_softmax(torch, fa)
+    if wk == "prefill_fp8" or all_legs:
+        prep["prefill_fp8"] = prepare_prefill_fp8(torch, fa)
+    if all_legs:
+        for name in OTHER_PREFILL:
+            prep[name] = prepare_prefill(torch, fa, name)
+        prep["standard_attention"] = prepare_standard_attention(torch)
+    torch.cuda.synchronize()
+    log("inputs of every leg resident in HBM")
+
+    def run(parts):
+        return time_leg(parts, K, W, settle, torch)
+
+    out_legs = {}
+    if "prefill" in prep:
+        w, parts = prep["prefill"]
+        t = run(parts)
+        flops = wl.algorithmic_flops(w)
+        mean = t.per_step(K)  # one kernel per step: its average launch duration over the timed region
+        out_legs["prefill"] = (w, t, {
+            "value": flops * K / (t.total_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "timing": Timing.stats(t.part_ms[0]),
+            "roofline": {"bound": "mfma", "achieved": round(flops / (mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill")}})
+        log(f"prefill done: {t.per_step(K):.4f} ms/launch (median {np.median(t.part_ms[0]):.4f})")
+    if "decode" in prep:
+        w, parts = prep["decode"]
+        t = run(parts)
+        nbytes = wl.algorithmic_bytes(w)
+        S = w.num_splits
+        part_bytes = w.B * w.H * w.Nq * S * (w.d + 2) * 4
+        split_bytes = nbytes - part_bytes - (w.B * w.H * w.Nq * (w.d * 2 + 4))  # q, k, v in; partials out
+        split_mean = float(np.mean(t.part_ms[0]))
+        value = nbytes * K / (t.total_ms * 1e-3) / 1e9
+        out_legs["decode"] = (w, t, {
+            "workload": w.name, "value": round(value, 1), "unit": "GB/s",
+            "ms_per_step": round(t.per_step(K), 4), "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
+            "timing": {"step": Timing.stats(t.step_ms), "split_kernel": Timing.stats(t.part_ms[0]),
+                       "combine_kernel": Timing.stats(t.part_ms[1])},
+            "step_frac_of_hbm_peak_at_median": round(nbytes / (np.median(t.step_ms) * 1e-3) / 1e9
+                                                     / PEAK_HBM_GBS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(split_bytes / (split_mean * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(split_bytes / (split_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode"), "kernel": "splitkv_decode_kernel",
+                         "avg_ms": round(split_mean, 4)}})
+        log(f"decode done: {t.per_step(K):.4f} ms/step (median {np.median(t.step_ms):.4f})")
+    if "rolling" in prep:
+        w, parts = prep["rolling"]
+        t = run(parts)
+        nbytes = wl.rolling_bytes(w)
+        S = w.num_splits
+        dec_bytes = 2 * w.rows * w.B * w.Hkv * w.d * 2 + w.B * w.H * w.d * 2 + w.B * w.H * S * (w.d + 2) * 4
+        dec_mean = float(np.mean(t.part_ms[1]))
+        value = nbytes * K / (t.total_ms * 1e-3) / 1e9
+        out_legs["rolling"] = (w, t, {
+            "workload": w.name, "value": round(value, 1), "unit": "GB/s",
+            "ms_per_step": round(t.per_step(K), 4), "frac_of_hbm_peak": round(value / PEAK_HBM_GBS, 4),
+            "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "d": w.d, "window": w.window, "sinks": w.sinks,
+                       "pos": w.pos, "cache_rows_read": w.rows, "num_splits": S},
+            "timing": {"step": Timing.stats(t.step_ms), "append_kernel": Timing.stats(t.part_ms[0]),
+                       "decode_kernel": Timing.stats(t.part_ms[1]), "combine_kernel": Timing.stats(t.part_ms[2])},
+            "roofline": {"bound": "hbm", "achieved": round(dec_bytes / (dec_mean * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(dec_bytes / (dec_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("rolling_decode"),
+                         "kernel": "splitkv_decode_kernel (rolling cache)", "avg_ms": round(dec_mean, 4)}})
+        log(f"rolling decode done: {t.per_step(K):.4f} ms/step")
+    if "softmax" in prep:
+        w, legs = prep["softmax"]
+        b = wl.softmax_bytes(w)
+        res = {n: run(p) for n, p in legs.items()}
+        sm = {"workload": w.name, "config": {"rows": w.rows, "n": w.n, "k": w.k, "dtype": "fp32"}}
+        for name, nbytes in (("softmax", b["softmax_online"]), ("topk", b["topk_fused"])):
+            t = res[name]
+            mean = t.per_step(K)
+            gbs = nbytes / (mean * 1e-3) / 1e9
+            sm[name] = {"ms_per_step": round(t.per_step(K), 4), "timing": Timing.stats(t.part_ms[0]),
+                        "bytes": nbytes, "value": round(gbs, 1), "unit": "GB/s",
+                        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name)}
+        ts, tt = (float(np.median(res[n].step_ms)) for n in ("torch_softmax", "torch_softmax_topk"))
+        sm["softmax"]["bytes_note"] = "two reads of x and one write of y (online normaliser)"
+        sm["softmax"]["byte_ratio_vs_three_pass"] = round(b["softmax_three_pass"] / b["softmax_online"], 3)
+        sm["softmax"]["torch_softmax_median_ms"] = round(ts, 4)
+        sm["softmax"]["speedup_vs_torch"] = round(ts / float(np.median(res["softmax"].part_ms[0])), 3)
+        sm["topk"]["bytes_note"] = "one read of x; k probabilities and indices written"
+        unfused = b["softmax_three_pass"] + w.rows * w.n * 4 + w.rows * w.k * 8
+        sm["topk"]["byte_ratio_vs_unfused"] = round(unfused / b["topk_fused"], 3)
+        sm["topk"]["torch_softmax_topk_median_ms"] = round(tt, 4)
+        sm["topk"]["speedup_vs_torch"] = round(tt / float(np.median(res["topk"].part_ms[0])), 3)
+        out_legs["softmax"] = (w, None, sm)
+        log(f"softmax done: {sm['softmax']['ms_per_step']:.4f} ms, top-k {sm['topk']['ms_per_step']:.4f} ms")
+    if "prefill_fp8" in prep:
+        w, parts = prep["prefill_fp8"]
+        t = run(parts)
+        flops = wl.algorithmic_flops(w)
+        mean = t.per_step(K)
+        value = flops * K / (t.total_ms * 1e-3) / 1e12
+        out_legs["prefill_fp8"] = (w, t, {
+            "workload": w.name, "value": round(value, 2), "unit": "TFLOP/s", "ms_per_step": round(t.per_step(K), 4),
+            "dtype": "fp8 e4m3 (bf16 out)", "timing": Timing.stats(t.part_ms[0]),
+            "roofline": {"bound": "mfma", "achieved": round(flops / (mean * 1e-3) / 1e12, 2),
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (mean * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill_fp8")}})
+        log(f"fp8 prefill done: {t.per_step(K):.4f} ms/launch")
+    others = {}
+    for name in OTHER_PREFILL:
+        if name not in prep:
+            continue
+        w, parts = prep[name]
+        t = run(parts)
+        flops = wl.algorithmic_flops(w)
+        value = flops * K / (t.total_ms * 1e-3) / 1e12
+        others[name] = {"workload": name, "value": round(value, 2), "unit": "TFLOP/s",
+                        "ms_per_step": round(t.per_step(K), 4), "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                        "timing": Timing.stats(t.part_ms[0]),
+                        "config": {"B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                                   "causal": w.causal, "head_window": "W on even heads" if w.head_window else None,
+                                   "softcap": w.softcap or None}}
+        log(f"{name} done: {t.per_step(K):.4f} ms/launch")
+    std = None
+    if "standard_attention" in prep:
+        w, parts = prep["standard_attention"]
+        t = time_leg(parts, 3, 1, 0.0, torch)
+        std = {"workload": w.name + " (first batch element)", "median_ms": round(float(np.median(t.step_ms)), 4)}
+        del prep["standard_attention"]
+        torch.cuda.empty_cache()
+        log(f"standard attention done: {std['median_ms']:.3f} ms")
+    dev = device_info(torch)
+    log("device info done")
+
+    main_key = {"prefill": "prefill", "decode": "decode", "prefill_fp8": "prefill_fp8", "rolling": "rolling",
+                "softmax": "softmax"}[wk]
+    if wk in ("rolling", "softmax"):
+        print(json.dumps({"leg": wk, **out_legs[main_key][2]}), flush=True)
         return
-    main_w, leg = None, None
-    decode = rolling = softmax = fp8 = others = None
-    if args.workload == "prefill":
-        main_w, leg = bench_prefill(torch, fa, args.steps, args.warmup)
-        print(f"[bench] prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
-        if not args.no_decode:
-            dw, decode = bench_decode(torch, fa, args.steps, args.warmup)
-            print(f"[bench] decode done: {decode['avg_ms']:.3f} ms/step", file=sys.stderr, flush=True)
-            rolling = bench_rolling(torch, fa, args.steps, args.warmup)
-            print(f"[bench] rolling decode done: {rolling['ms_per_step']:.4f} ms/step", file=sys.stderr,
-                  flush=True)
-            softmax = bench_softmax(torch, fa, args.steps, args.warmup)
-            print(f"[bench] softmax done: {softmax['softmax']['ms_per_step']:.4f} ms, top-k "
-                  f"{softmax['topk']['ms_per_step']:.4f} ms", file=sys.stderr, flush=True)
-            _, fp8 = bench_prefill_fp8(torch, fa, args.steps, args.warmup)
-            print(f"[bench] fp8 prefill done: {fp8['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
-            others = {}
-            for name in OTHER_PREFILL:
-                others[name] = bench_prefill_config(torch, fa, name, args.steps, args.warmup)
-                print(f"[bench] {name} done: {others[name]['ms_per_step']:.4f} ms/launch", file=sys.stderr,
-                      flush=True)
-        value, unit = leg["value"], "TFLOP/s"
-    elif args.workload == "prefill_fp8":
-        main_w, leg = bench_prefill_fp8(torch, fa, args.steps, args.warmup)
-        value, unit = leg["value"], "TFLOP/s"
-        print(f"[bench] fp8 prefill done: {leg['avg_ms']:.3f} ms/launch", file=sys.stderr, flush=True)
-    else:
-        main_w, leg = bench_decode(torch, fa, args.steps, args.warmup)
-        value, unit = leg["value"], "GB/s"
-        print(f"[bench] decode done: {leg['avg_ms']:.3f} ms/step", file=sys.stderr, flush=True)
-
-    w = main_w
+    w, t, leg = out_legs[main_key]
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(leg["total_ms"] / args.steps, 4),
+        "metric": METRIC, "value": round(leg["value"], 2), "unit": leg["unit"], "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(t.per_step(K), 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8" if args.workload == "prefill_fp8" else "bf16",
+        "dtype": "fp8" if wk == "prefill_fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                    "causal": w.causal, "num_splits": w.num_splits or None, "parallelism": "none (1 GPU)"},
+        "timing": {"per_launch": leg["timing"] if "step" not in leg.get("timing", {}) else leg["timing"]["step"],
+                   "settle_ms": settle,
+                   "method": "value and ms_per_step: one pair of HIP events on the launch stream around the "
+                             "K back-to-back timed steps; per_launch: a second pass of K steps with events "
+                             "before and after every kernel; before its warm-up each leg runs untimed for "
+                             "settle_ms of wall time (an idle GPU needs tens of milliseconds to reach its "
+                             "working clock)"},
         "roofline": leg["roofline"],
     }
-    if decode is not None:
-        out["decode"] = {"workload": DECODE, "value": round(decode["value"], 1), "unit": "GB/s",
-                         "ms_per_step": round(decode["total_ms"] / args.steps, 4),
-                         "frac_of_hbm_peak": round(decode["value"] / PEAK_HBM_GBS, 4),
-                         "roofline": decode["roofline"]}
-    if rolling is not None:
-        out["rolling"] = rolling
-    if softmax is not None:
-        out["softmax"] = softmax
-    if fp8 is not None:
-        w8 = wl.FP8_PREFILL
-        out["prefill_fp8"] = {"workload": w8.name, "value": round(fp8["value"], 2), "unit": "TFLOP/s",
-                              "ms_per_step": round(fp8["total_ms"] / args.steps, 4), "dtype": "fp8 e4m3 (bf16 out)",
-                              "roofline": fp8["roofline"]}
-    if others is not None:
+    if wk == "prefill" and std is not None:
+        ours_b1 = float(np.median(t.part_ms[0])) / w.B
+        std["ours_median_ms_per_batch_element"] = round(ours_b1, 4)
+        std["speedup"] = round(std["median_ms"] / ours_b1, 2)
+        out["standard_attention"] = std
+    for key in ("decode", "rolling", "softmax", "prefill_fp8"):
+        if key in out_legs and key != main_key:
+            out[key] = out_legs[key][2]
+    if others:
         out["other_prefill"] = others
+    out["device"] = dev
+    out["pages_context"] = PAGES_CONTEXT
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
-        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+        log("cpu baseline done")
     print(json.dumps(out), flush=True)
 
 

@@ -9,6 +9,10 @@ namespace fa {
 
 // bf16 tiled forward (MFMA).  split: write per-split partials instead of O.
 int launch_fwd_bf16(const FwdParams &p, int d, bool split, hipStream_t stream);
+// bf16 tiled forward with 64 query rows per wave (d = 128, unsplit), for
+// grids of at least 512 blocks of 256 query rows.
+bool fwd_bf16_wide_applies(const FwdParams &p, int d);
+int launch_fwd_bf16_wide(const FwdParams &p, hipStream_t stream);
 // fp8 (E4M3) tiled forward (MFMA), bf16 output.  c_log2 > 0 multiplies the
 // integer-exact fp8 dot products into base-2 score units; out_scale
 // multiplies O; qflip is xor-ed into every 4 bytes of Q (0x80808080 negates Q).

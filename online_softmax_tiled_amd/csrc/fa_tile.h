@@ -43,6 +43,29 @@ __device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t nby
         : "memory");
 }
 
+// The same load with the LDS destination given as a wave-uniform LDS byte
+// address (no generic-to-LDS pointer conversion at each call).
+__device__ __forceinline__ void buffer_load_lds16_at(const void *base, uint32_t nbytes, uint32_t lds_addr, int voff,
+                                                     uint32_t soff) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 rsrc;
+    rsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    rsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+    rsrc[2] = __builtin_amdgcn_readfirstlane(nbytes);                         // num_records
+    rsrc[3] = 0x00020000u;                                                    // raw buffer, dword data
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m), "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff))
+        : "memory");
+}
+
 // Workgroup barrier for LDS traffic only: it waits for this wave's LDS
 // reads and writes but not for its loads still streaming into LDS, which
 // __syncthreads() also drains (its fence counts them as LDS writes).  A
