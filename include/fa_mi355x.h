@@ -67,7 +67,9 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1, /* bad size, null pointer, bad flag combination */
     FA_ERR_UNSUPPORTED = -2, /* valid request with no kernel (d, dtype)       */
-    FA_ERR_HIP = -3          /* the HIP runtime reported a launch failure     */
+    FA_ERR_HIP = -3,         /* the HIP runtime reported a launch failure     */
+    FA_ERR_SCRATCH_LIMIT = -4 /* fa_splitkv_attention_static: partials exceed
+                                 FA_STATIC_SCRATCH_BYTES                      */
 } fa_status;
 
 typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
@@ -294,6 +296,35 @@ int fa_softmax(const void *x, void *y, float *lse, int64_t rows, int64_t n, int 
  */
 int fa_softmax_topk(const void *x, float *probs, int32_t *indices, float *lse, int64_t rows,
                     int64_t n, int k, int dtype, fa_stream_t stream);
+
+/*
+ * fa_splitkv_attention_static -- split-KV attention (fa_fwd_splitkv followed
+ * by fa_combine) that allocates nothing and takes no workspace: the
+ * per-split partials live in a fixed device array inside the library, one
+ * per GPU, of FA_STATIC_SCRATCH_BYTES.  For callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ * Arguments as fa_fwd_splitkv, plus o ([B,H,Nq,d] in out_dtype,
+ * FA_DTYPE_BF16 or FA_DTYPE_FP32) and lse (fp32 [B,H,Nq] or NULL) as
+ * fa_combine writes them; q, k, v bf16.  The partials need
+ * B*H*Nq*num_splits*(d+2)*4 bytes; a larger request returns
+ * FA_ERR_SCRATCH_LIMIT and launches nothing.  The first call on a device
+ * looks up that device's array (hipGetSymbolAddress) and keeps its address;
+ * the array itself is held until the process ends.  Every call on one GPU
+ * uses the same array: calls that overlap on one GPU (on different streams,
+ * or from several host threads without ordering) race and give wrong
+ * results.  Calls ordered on one stream are fine; every partial is written
+ * before it is read, so nothing needs clearing between calls.
+ * Errors: as fa_fwd_splitkv and fa_combine, plus FA_ERR_SCRATCH_LIMIT, and
+ * FA_ERR_HIP if the device array cannot be looked up.
+ */
+#define FA_STATIC_SCRATCH_BYTES (8u << 20) /* 8 MiB per GPU */
+
+int fa_splitkv_attention_static(const void *q, const void *k, const void *v, void *o, float *lse,
+                                int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                                float scale, int causal, int window, float softcap, int num_splits,
+                                int out_dtype, fa_stream_t stream);
 
 /* Human-readable name of a status code (static storage). */
 const char *fa_status_string(int status);

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -143,6 +145,32 @@ fa_fwd_args make_args(int dtype, const void *q, const void *k, const void *v, vo
     return a;
 }
 
+// Split-KV partials of fa_splitkv_attention_static: a fixed device array,
+// one copy per GPU the library runs on, held until the process ends.  In
+// host code `scratch` names a host-side stand-in: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchFloats = FA_STATIC_SCRATCH_BYTES / sizeof(float);
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(float **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_HIP;
+        g_scratch_dev[dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch_dev[dev];
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -270,12 +298,39 @@ int fa_softmax_topk(const void *x, float *probs, int32_t *indices, float *lse, i
     return fa::launch_softmax_topk(x, probs, indices, lse, rows, n, k, dtype, reinterpret_cast<hipStream_t>(stream));
 }
 
+int fa_splitkv_attention_static(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                                int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                                int window, float softcap, int num_splits, int out_dtype, fa_stream_t stream) {
+    if (num_splits < 1) return FA_ERR_INVALID_ARG;
+    if (out_dtype != FA_DTYPE_BF16 && out_dtype != FA_DTYPE_FP32) return FA_ERR_INVALID_ARG;
+    fa_fwd_args a = make_args(FA_DTYPE_BF16, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window,
+                              softcap, stream);
+    FwdParams p;
+    const int rc = validate_fwd(a, p);
+    if (rc != FA_OK) return rc;
+    if (!aligned(o, out_dtype == FA_DTYPE_BF16 ? 2 : 4)) return FA_ERR_INVALID_ARG;
+    const int64_t rows = mul(mul(B, H), Nq);
+    if (rows == 0) return FA_OK;
+    // Partials: o_part [rows, S, d], then m_part and l_part [rows, S].
+    const int64_t parts = mul(rows, num_splits);
+    if (mul(parts, d + 2) > (int64_t)kScratchFloats) return FA_ERR_SCRATCH_LIMIT;
+    float *base = nullptr;
+    const int src = scratch_address(&base);
+    if (src != FA_OK) return src;
+    float *o_part = base, *m_part = base + parts * d, *l_part = m_part + parts;
+    const int r1 = run_splitkv(p, o_part, m_part, l_part, num_splits, d, stream);
+    if (r1 != FA_OK) return r1;
+    return fa::launch_combine(o_part, m_part, l_part, o, lse, rows, num_splits, (int)d, out_dtype,
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
 const char *fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";
         case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this head size or shape";
         case FA_ERR_HIP: return "FA_ERR_HIP: HIP kernel launch failed";
+        case FA_ERR_SCRATCH_LIMIT: return "FA_ERR_SCRATCH_LIMIT: partials exceed the static scratch";
         default: return "unknown fa_status";
     }
 }

@@ -27,7 +27,9 @@ FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 FA_MAX_HEAD_WINDOWS = 256
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
-            "fa_decode_rolling", "fa_softmax", "fa_softmax_topk", "fa_status_string")
+            "fa_decode_rolling", "fa_softmax", "fa_softmax_topk", "fa_splitkv_attention_static", "fa_status_string")
+FA_ERR_SCRATCH_LIMIT = -4
+FA_STATIC_SCRATCH_BYTES = 8 << 20
 FA_MAX_TOPK = 64
 
 
@@ -87,8 +89,10 @@ def load_library():
                                       f32, f32, ci, vp]
     lib.fa_softmax.argtypes = [vp, vp, vp, i64, i64, ci, vp]
     lib.fa_softmax_topk.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci, vp]
+    lib.fa_splitkv_attention_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, ci, ci,
+                                                f32, ci, ci, vp]
     for name in ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_combine", "fa_kv_append",
-                 "fa_decode_rolling", "fa_softmax", "fa_softmax_topk"):
+                 "fa_decode_rolling", "fa_softmax", "fa_softmax_topk", "fa_splitkv_attention_static"):
         getattr(lib, name).restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -187,6 +191,14 @@ def fa_softmax_topk(x, probs, indices, lse, rows, n, k, dtype, stream=None):
     _check(load_library().fa_softmax_topk(_ptr(x), _ptr(probs), _ptr(indices), _ptr(lse), rows, n, int(k),
                                            int(dtype), _stream(stream)),
            "fa_softmax_topk")
+
+def fa_splitkv_attention_static(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, softcap, num_splits,
+                                out_dtype, stream=None):
+    _check(load_library().fa_splitkv_attention_static(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, Nq, Nk, d, float(scale), int(causal),
+        int(window), float(softcap), int(num_splits), int(out_dtype), _stream(stream)),
+        "fa_splitkv_attention_static")
+
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, q_descale, k_descale, v_descale, causal, window,
                stream=None):

@@ -264,3 +264,16 @@ def test_binding_checks_head_window_length_and_alignment():
     with pytest.raises(ValueError, match="aligned"):
         fa._check_aligned(x[1:], 16, "q")
     fa._check_aligned(x[8:], 16, "q")
+
+
+def test_static_scratch_entry_point_validation():
+    # Refused before any HIP call: these run without a GPU.
+    lib = fa.load_library()
+    args = [FAKE, FAKE, FAKE, FAKE, None, 4, 32, 8, 32, 64, 128, 0.1, 0, 0, 0.0]
+    assert lib.fa_splitkv_attention_static(*args, 0, fa.FA_DTYPE_BF16, FAKE) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_splitkv_attention_static(*args, 4, 9, FAKE) == fa.FA_ERR_INVALID_ARG   # out dtype
+    # 4096 rows x 64 splits x (128 + 2) fp32 partials exceed the 8 MiB scratch
+    assert lib.fa_splitkv_attention_static(*args, 64, fa.FA_DTYPE_BF16, FAKE) == fa.FA_ERR_SCRATCH_LIMIT
+    assert "scratch" in fa.fa_status_string(fa.FA_ERR_SCRATCH_LIMIT)
+    a2 = list(args); a2[2] = None
+    assert lib.fa_splitkv_attention_static(*a2, 4, fa.FA_DTYPE_BF16, FAKE) == fa.FA_ERR_INVALID_ARG
