@@ -75,6 +75,20 @@ __device__ __forceinline__ bf16x8 p_operand(const f32x16 &s, int ks) {
     return __builtin_bit_cast(bf16x8, w);
 }
 
+// Maximum of the 16 scores a lane holds for one row, with v_max3_f32 (the
+// plain fmaxf chain adds a quieting max per input in IEEE mode).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+__device__ __forceinline__ float max16(const f32x16 &s) {
+    const float a = max3(s[0], s[1], s[2]), b = max3(s[3], s[4], s[5]), c = max3(s[6], s[7], s[8]);
+    const float d = max3(s[9], s[10], s[11]), e = max3(s[12], s[13], s[14]);
+    return max3(max3(a, b, c), max3(d, e, s[15]), a);
+}
+
 __device__ __forceinline__ void pack_weights(f32x16 &s) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -87,6 +101,7 @@ struct WideWave {
     bf16x8 qf[2][D / 16];       // Q^T operand per row block and 16-dim step
     f32x16 oacc[2][D / 32];     // O^T accumulators per row block and 32-dim block
     float m[2], l[2];           // reference maximum (log2 units); this lane's half of the normaliser
+    float mu[2];                // the reference the weights are taken against (0 while m is -inf)
     float lx[2];                // FIXED: this lane's half of the sum of the fp32 weights (for lse)
     float c_log2, scale, softcap;
     // Lane-dependent offsets and mask bounds are recomputed from the lane id
@@ -182,17 +197,11 @@ struct WideWave {
         }
     }
 
-    // Online softmax of one 32-key half whose first key is `key` (absolute):
-    // masks (if MASK; the wave's rows start at query row `row0` of a head
-    // with window W), row maximum, lazy move of the reference maximum
-    // (wave-uniform; returns whether it moved and the factors), weights
-    // rounded to bf16 as the P^T operands.  FIXED (soft-capped scores, |z|
-    // <= softcap <= kFixedMaxCap): the reference maximum stays 0 and the
-    // maximum, the move and the rescale are skipped.
+    // Scores of one 32-key half whose first key is `key` (absolute) made
+    // ready for the weights: scale and soft-cap (EXPLICIT), masks (if MASK;
+    // the wave's rows start at query row `row0` of a head with window W).
     template <bool MASK>
-    __device__ __forceinline__ bool softmax(f32x16 (&s)[2], int64_t key, const FwdParams &pr, int64_t row0, int W,
-                                            float (&alpha)[2]) {
-        float mt[2];
+    __device__ __forceinline__ void prepare(f32x16 (&s)[2], int64_t key, const FwdParams &pr, int64_t row0, int W) {
         int lane = lane_id();
         if (MASK) asm volatile("" : "+v"(lane));
 #pragma unroll
@@ -220,12 +229,21 @@ struct WideWave {
                     if (!((uint32_t)(c - base) < span)) s[rb][j] = kNegInf;
                 }
             }
-            if (FIXED) continue;
-            float x = s[rb][0];
-#pragma unroll
-            for (int j = 1; j < 16; ++j) x = fmaxf(x, s[rb][j]);
-            mt[rb] = row_max(EXPLICIT ? x : x * c_log2);
         }
+    }
+
+    // Online softmax of one 32-key half: lazy move of the reference maximum
+    // (wave-uniform; returns whether it moved and the factors), weights
+    // rounded to bf16 as the P^T operands.  The reference moves only when a
+    // weight against it would exceed 2^TAU, which each lane sees from the
+    // maximum of its own 16 scores; only then is the row maximum taken across
+    // the lane pair and the reference moved.  FIXED (soft-capped scores, |z|
+    // <= softcap <= kFixedMaxCap): the reference maximum stays 0 and the
+    // maximum, the move and the rescale are skipped.
+    template <bool MASK>
+    __device__ __forceinline__ bool softmax(f32x16 (&s)[2], int64_t key, const FwdParams &pr, int64_t row0, int W,
+                                            float (&alpha)[2]) {
+        prepare<MASK>(s, key, pr, row0, W);
         if (FIXED) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -241,24 +259,40 @@ struct WideWave {
             }
             return false;
         }
-        const bool grow = (mt[0] > m[0] + TAU) || (mt[1] > m[1] + TAU);
-        const bool move = __builtin_amdgcn_ballot_w64(grow) != 0;
+        float x[2];
+        bool grow = false;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const float m_new = move ? fmaxf(m[rb], mt[rb]) : m[rb];
-            const float m_use = m_new == kNegInf ? 0.0f : m_new;
-            alpha[rb] = fast_exp2(m[rb] - m_use);
-            m[rb] = m_new;
+            x[rb] = max16(s[rb]);
+            // NaN (a lane whose keys are all masked, reference still -inf) is no growth.
+            const float over = EXPLICIT ? x[rb] - m[rb] : fmaf(x[rb], c_log2, -m[rb]);
+            grow = grow || over > TAU;
+        }
+        const bool move = __builtin_amdgcn_ballot_w64(grow) != 0;
+        if (move) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const float mt = row_max(EXPLICIT ? x[rb] : x[rb] * c_log2);
+                const float m_new = fmaxf(m[rb], mt);
+                const float m_use = m_new == kNegInf ? 0.0f : m_new;
+                alpha[rb] = fast_exp2(m[rb] - m_use);  // 0 while m is -inf (O and l are still 0)
+                m[rb] = m_new;
+                mu[rb] = m_use;
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                s[rb][j] = EXPLICIT ? fast_exp2(s[rb][j] - m_use) : fast_exp2(fmaf(s[rb][j], c_log2, -m_use));
+                s[rb][j] = EXPLICIT ? fast_exp2(s[rb][j] - mu[rb]) : fast_exp2(fmaf(s[rb][j], c_log2, -mu[rb]));
             // The normaliser sums the fp32 weights, before their rounding to
             // bf16 for P.V.
             float rs[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 rs[i] = (s[rb][4 * i] + s[rb][4 * i + 1]) + (s[rb][4 * i + 2] + s[rb][4 * i + 3]);
-            l[rb] = fmaf(l[rb], alpha[rb], (rs[0] + rs[1]) + (rs[2] + rs[3]));
+            const float r = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            l[rb] = move ? fmaf(l[rb], alpha[rb], r) : l[rb] + r;
             pack_weights(s[rb]);
         }
         return move;
@@ -417,6 +451,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
             st.qf[rb][ds] = __builtin_bit_cast(bf16x8, x);
         }
         st.m[rb] = FIXED ? 0.0f : kNegInf;
+        st.mu[rb] = 0.0f;
         st.l[rb] = 0.0f;
         st.lx[rb] = 0.0f;
 #pragma unroll
