@@ -59,8 +59,8 @@ PREFILL = "bf16_causal_b4_h32_n4096_d128"
 DECODE = "bf16_splitkv_decode_b16_h32kv8_nk32768_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
-    "prefill": ["online_softmax_tiled_amd/csrc/fa_fwd_bf16.hip", "online_softmax_tiled_amd/csrc/fa_tile.h",
-                "online_softmax_tiled_amd/csrc/fa_device.h"],
+    "prefill": ["online_softmax_tiled_amd/csrc/fa_fwd_bf16_wide.hip", "online_softmax_tiled_amd/csrc/fa_bf16_tile.h",
+                "online_softmax_tiled_amd/csrc/fa_tile.h", "online_softmax_tiled_amd/csrc/fa_device.h"],
     "decode": ["online_softmax_tiled_amd/csrc/fa_splitkv.hip", "online_softmax_tiled_amd/csrc/fa_device.h"],
     "prefill_fp8": ["online_softmax_tiled_amd/csrc/fa_fwd_fp8.hip", "online_softmax_tiled_amd/csrc/fa_tile.h",
                     "online_softmax_tiled_amd/csrc/fa_device.h"],
@@ -458,7 +458,7 @@ PROFILE_RUNS = {
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
                        "python bench.py --copy-calibration",
 }
-KERNELS = {"prefill": "fwd_bf16_kernel<128, false, false, false, false, 8>", "decode": "splitkv_decode_kernel<128, 4, false>",
+KERNELS = {"prefill": "fwd_bf16_wide_kernel<false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
            "combine": "combine_few_kernel<128, 16>", "prefill_fp8": "fwd_fp8_kernel<128>",
            "rolling_decode": "splitkv_decode_kernel<128, 4, false>", "kv_append": "kv_append_kernel<128>",
            "softmax": "softmax_kernel<false, 4>", "topk": "softmax_topk_kernel<false, 4>",
@@ -537,7 +537,7 @@ def summarize_profiles(d):
     flops = wl.algorithmic_flops(wp)
     rb, wb = hbm["prefill"]
     qkv_bytes = 2 * (wp.B * wp.H * wp.Nq * wp.d + 2 * wp.B * wp.Hkv * wp.Nk * wp.d)
-    md = f"""# fwd_bf16_kernel on the causal prefill workload (B=4, H=32, Nq=Nk=4096, d=128, bf16)
+    md = f"""# fwd_bf16_wide_kernel on the causal prefill workload (B=4, H=32, Nq=Nk=4096, d=128, bf16)
 
 Command (run from the repository root on one MI355X):
 
