@@ -90,6 +90,7 @@ int run_fwd(const fa_fwd_args &a) {
     hipStream_t s = reinterpret_cast<hipStream_t>(a.stream);
     if (a.dtype == FA_DTYPE_FP32) return fa::launch_fwd_f32(p, (int)a.d, s);
     if (fa::fwd_bf16_wide_applies(p, (int)a.d)) return fa::launch_fwd_bf16_wide(p, s);
+    if (fa::fwd_bf16_splitk_applies(p, (int)a.d)) return fa::launch_fwd_bf16_splitk(p, (int)a.d, s);
     return fa::launch_fwd_bf16(p, (int)a.d, false, s);
 }
 

@@ -13,6 +13,10 @@ int launch_fwd_bf16(const FwdParams &p, int d, bool split, hipStream_t stream);
 // grids of at least 512 blocks of 256 query rows.
 bool fwd_bf16_wide_applies(const FwdParams &p, int d);
 int launch_fwd_bf16_wide(const FwdParams &p, hipStream_t stream);
+// bf16 tiled forward for small grids: 4 waves per 32 query rows, each on a
+// quarter of the keys, merged in LDS (d in {32, 64, 128}, unsplit).
+bool fwd_bf16_splitk_applies(const FwdParams &p, int d);
+int launch_fwd_bf16_splitk(const FwdParams &p, int d, hipStream_t stream);
 // fp8 (E4M3) tiled forward (MFMA), bf16 output.  c_log2 > 0 multiplies the
 // integer-exact fp8 dot products into base-2 score units; out_scale
 // multiplies O; qflip is xor-ed into every 4 bytes of Q (0x80808080 negates Q).
