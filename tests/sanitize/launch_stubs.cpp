@@ -19,6 +19,8 @@ namespace fa {
 int launch_fwd_bf16(const FwdParams &, int, bool, hipStream_t) { reached("launch_fwd_bf16"); }
 bool fwd_bf16_wide_applies(const FwdParams &, int) { reached("fwd_bf16_wide_applies"); }
 int launch_fwd_bf16_wide(const FwdParams &, hipStream_t) { reached("launch_fwd_bf16_wide"); }
+bool fwd_bf16_splitk_applies(const FwdParams &, int) { reached("fwd_bf16_splitk_applies"); }
+int launch_fwd_bf16_splitk(const FwdParams &, int, hipStream_t) { reached("launch_fwd_bf16_splitk"); }
 int launch_fwd_fp8(const FwdParams &, int, float, float, uint32_t, hipStream_t) { reached("launch_fwd_fp8"); }
 int launch_fwd_f32(const FwdParams &, int, hipStream_t) { reached("launch_fwd_f32"); }
 int launch_splitkv_decode(const FwdParams &, int, hipStream_t) { reached("launch_splitkv_decode"); }
