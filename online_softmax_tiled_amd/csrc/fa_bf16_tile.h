@@ -65,21 +65,54 @@ struct TileLoader128 {
     // Load u fills LDS chunk slots q*64 + lane (q = 4 lw + u) of a tile:
     // row rr = 16 lw + 4 u + lane/16, slot sl = lane % 16, which holds
     // chunk sl ^ (rr % 16) = sl ^ (lane/16) ^ 4u of K, or sl ^ 4 (lane/16)
-    // of V (xor is its own inverse).  Byte offset: row base + 16 * chunk,
-    // i.e. a per-lane base (xor-ed with 64 u for K) plus 1024 u; the tile's
-    // offset within the head goes in the scalar offset.
+    // of V (xor is its own inverse).  Byte offset in the head: the tile's
+    // offset (scalar), a per-lane base (xor-ed with 64 u for K) and 1024 u.
+    // The four loads of a wave share one M0 value: the 1024 u steps go in
+    // the instruction offset, which the hardware adds to both the global
+    // and the LDS address.  head_bytes = 0 makes every load read zeros
+    // without touching memory (used when there is no next tile, so that
+    // the loads need no branch).
     template <bool IS_V>
     __device__ __forceinline__ void load(const void *base, uint32_t head_bytes, uint32_t tile, int64_t kt) const {
         int lane = lane_id();
         asm volatile("" : "+v"(lane));
         const int x = lane >> 4, sl = lane & 15;
         const uint32_t g0 = (uint32_t)((16 * lw + x) * 256 + 16 * (IS_V ? (sl ^ (4 * x)) : (sl ^ x)));
-        const uint32_t toff = (uint32_t)kt * (uint32_t)(D * 2);
-#pragma unroll
-        for (int u = 0; u < L::LPW; ++u) {
-            const uint32_t flip = IS_V ? 0u : (uint32_t)(64 * u);
-            buffer_load_lds16_at(base, head_bytes, tile + (uint32_t)((4 * lw + u) * 1024),
-                                 (int)((g0 ^ flip) + 1024u * u), toff);
+        const uint64_t a = reinterpret_cast<uint64_t>(base);
+        u32x4 rsrc;
+        rsrc[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+        rsrc[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+        rsrc[2] = __builtin_amdgcn_readfirstlane(head_bytes);                     // num_records
+        rsrc[3] = 0x00020000u;                                                    // raw buffer, dword data
+        const uint32_t m = __builtin_amdgcn_readfirstlane(tile + (uint32_t)(4 * lw * 1024));
+        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)kt * (uint32_t)(D * 2));
+        uint32_t saved;
+        if (IS_V) {
+            asm volatile(
+                "s_mov_b32 %0, m0\n\t"
+                "s_mov_b32 m0, %1\n\t"
+                "s_nop 0\n\t"
+                "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+                "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds\n\t"
+                "buffer_load_dwordx4 %2, %3, %4 offen offset:2048 lds\n\t"
+                "buffer_load_dwordx4 %2, %3, %4 offen offset:3072 lds\n\t"
+                "s_mov_b32 m0, %0"
+                : "=&s"(saved)
+                : "s"(m), "v"(g0), "s"(rsrc), "s"(so)
+                : "memory");
+        } else {
+            asm volatile(
+                "s_mov_b32 %0, m0\n\t"
+                "s_mov_b32 m0, %1\n\t"
+                "s_nop 0\n\t"
+                "buffer_load_dwordx4 %2, %6, %7 offen lds\n\t"
+                "buffer_load_dwordx4 %3, %6, %7 offen offset:1024 lds\n\t"
+                "buffer_load_dwordx4 %4, %6, %7 offen offset:2048 lds\n\t"
+                "buffer_load_dwordx4 %5, %6, %7 offen offset:3072 lds\n\t"
+                "s_mov_b32 m0, %0"
+                : "=&s"(saved)
+                : "s"(m), "v"(g0), "v"(g0 ^ 64u), "v"(g0 ^ 128u), "v"(g0 ^ 192u), "s"(rsrc), "s"(so)
+                : "memory");
         }
     }
 };

@@ -16,15 +16,28 @@
 // processes each 64-key tile as two halves of 32 keys, and keeps its
 // lane-dependent LDS and load offsets out of registers (recomputed per use).
 //
-// Workgroup: 8 waves in two groups of 4.  A group is one block of 256
-// query rows of one (batch, head) with its own K and V tiles in LDS (64 KiB
-// per group); the two groups of a workgroup take two heads' blocks
-// with the same query tile, so they see the same number of key tiles.
-// Wave i of group 0 and wave i of group 1 share SIMD i and ping-pong: while
-// one runs a matrix phase (P.V of the previous 32-key half, then the scores
-// of the next one; MFMA and LDS reads only) the other runs the vector phase
-// (masks, row maximum, exp2, row sum, bf16 packing), and the roles swap at
-// each workgroup barrier.  Within a group, K and V tiles go from HBM straight
+// A group is 4 waves on one block of 256 query rows of one (batch, head)
+// with its own K and V tiles in LDS (64 KiB).  Each wave alternates a
+// matrix phase (P.V of the previous 32-key half, then the scores of the
+// next one; MFMA and LDS reads only) and a vector phase (masks, exp2, row
+// sum, bf16 packing), with a group barrier after each.  Two waves share
+// each SIMD, in one of two workgroup forms (template parameter NG):
+//   * NG = 1: a workgroup is one group, two workgroups per CU.  They run
+//     independently; a workgroup that ends leaves the CU to the other one
+//     while the next starts loading.  Used when every head sees the same
+//     keys (no windows) and scores are not soft-capped.
+//   * NG = 2: a workgroup is two groups (8 waves) taking two heads' blocks
+//     with the same query tile; wave i of group 0 and wave i of group 1
+//     share SIMD i and ping-pong (group 1 runs one phase behind), so the
+//     roles swap at each workgroup barrier.  Faster where the vector phase
+//     is long (soft-capped scores: a tanh per score) or where heads differ
+//     in length (windows on some heads): the pairing puts heads of equal
+//     length side by side.
+// Unless scores are soft-capped, a wave raises its priority for its matrix
+// phases: the vector work of the other wave on the SIMD then fills the
+// gaps between MFMAs instead of delaying them (the older wave wins the
+// issue arbitration otherwise).
+// Within a group, K and V tiles go from HBM straight
 // into LDS (direct loads by the group's 4 waves, 16 keys each), row-major
 // with swizzles against bank conflicts (fa_bf16_tile.h); the V^T operand of
 // P.V is read from the row-major V tile with transposing LDS reads, so V is
@@ -167,14 +180,14 @@ struct WideWave {
     }
 
     // A whole matrix phase in one scheduling region: P.V of the previous
-    // half (weights in s) then the scores of the next half (into s), the
-    // first K operands read while the last P.V products issue.
+    // half (weights in s) then the scores of the next half (into s).  16
+    // transposing reads feeding one MFMA each, 8 issued ahead, then 8 K
+    // reads feeding two, 4 ahead.
     __device__ __forceinline__ void pv_scores(const char *vt, int hh_pv, const char *kt, int hh_s, f32x16 (&s)[2]) {
         pv<false>(vt, hh_pv, s);
         scores<false>(kt, hh_s, s);
-        // 16 transposing reads feeding one MFMA each, then 8 K reads feeding two.
-        sched_read_mfma_pipeline<D / 32 * 4, 1, 4>();
-        sched_read_mfma_pipeline<D / 16, 2, 2>();
+        sched_read_mfma_pipeline<D / 32 * 4, 1, 8>();
+        sched_read_mfma_pipeline<D / 16, 2, 4>();
     }
 
     // FIXED: this lane's sum of its bf16 weights (dot2 with (1, 1)), which
@@ -388,9 +401,9 @@ __device__ __forceinline__ int block_tiles(const FwdParams &p, int64_t q0, int64
     return hi_last > lo_first ? (int)((hi_last - lo_first + BN - 1) / BN) : 0;
 }
 
-template <bool EXPLICIT, bool CAP, bool FIXED>
-__global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p, const PairMap pm) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * GROUP_TILES * L::TILE];
+template <int NG, bool EXPLICIT, bool CAP, bool FIXED>
+__global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const FwdParams p, const PairMap pm) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[NG * GROUP_TILES * L::TILE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,7 +411,16 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
     const int l32 = lane & 31, hf = lane >> 5;
 
     int ua, ha, ub, hb, qtile;
-    const bool has_b = pm.decode(blockIdx.x, p.causal, ua, ha, ub, hb, qtile);
+    bool has_b = false;
+    if (NG == 2) {
+        has_b = pm.decode(blockIdx.x, p.causal, ua, ha, ub, hb, qtile);
+    } else {
+        // One block per workgroup, in the XCD-aware order of decode_block.
+        const Work wk = decode_block(p, pm.n_qtiles);
+        qtile = wk.qtile;
+        ua = wk.b * (int)p.Hkv + wk.h / pm.rep;
+        ha = wk.h % pm.rep;
+    }
     const bool active = grp == 0 || has_b;
     const int unit = grp == 0 ? ua : ub;
     const int b = unit / (int)p.Hkv;
@@ -415,7 +437,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
     if (!active) kbeg = 0;
     // Both groups run the longer of the two tile loops (the barriers pair up).
     int nsteps = ntiles;
-    {
+    if (NG == 2) {
         const int h_o = grp == 0 ? (ub % (int)p.Hkv) * pm.rep + hb : (ua % (int)p.Hkv) * pm.rep + ha;
         const bool act_o = grp == 1 || has_b;
         int64_t kb_o;
@@ -475,6 +497,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
         }
     }
 
+    // Matrix phases at raised priority (not with the tanh-heavy vector phase
+    // of soft-capped scores).
+    constexpr bool PRIO = !CAP;
     TileLoader128 ld;
     ld.lw = wi;
     const uint32_t head_bytes = (uint32_t)(Nk * D * 2);
@@ -486,7 +511,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
     }
     __builtin_amdgcn_s_waitcnt(0);  // also the Q loads
     lds_barrier();
-    if (grp == 1) lds_barrier();  // group 1 runs one phase behind group 0
+    if (NG == 2 && grp == 1) lds_barrier();  // group 1 runs one phase behind group 0
 
     f32x16 s[2];          // scores of a half, then (packed) its weights
     bool have_p = false;  // s holds weights of the previous half, not yet multiplied into O
@@ -512,7 +537,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
         const char *const vprev = vt0 + ((j + 1) & 1) * TILE_BYTES;
         const int key0 = j * BN;  // relative to kbeg
         // ---- M(2j)
-        if (more) ld.load<false>(K, head_bytes, glds_at + (KT0 + ((j + 1) & 1)) * TILE_BYTES, kt + BN);
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
+        ld.load<false>(K, more ? head_bytes : 0u, glds_at + (KT0 + ((j + 1) & 1)) * TILE_BYTES, more ? kt + BN : 0);
         const bool live0 = mine && (!MASK || (key0 < whi && key0 + HALF > wlo));
         if (MASK) {
             if (have_p) st.pv(vprev, 1, s);
@@ -522,6 +548,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
         }
         lds_barrier();
         // ---- V(2j)
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
         have_p = live0;
         if (live0) {
             float alpha[2];
@@ -536,7 +563,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
         }
         lds_barrier();
         // ---- M(2j+1)
-        if (more) ld.load<true>(V, head_bytes, glds_at + (VT0 + ((j + 1) & 1)) * TILE_BYTES, kt + BN);
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
+        ld.load<true>(V, more ? head_bytes : 0u, glds_at + (VT0 + ((j + 1) & 1)) * TILE_BYTES, more ? kt + BN : 0);
         const bool live1 = mine && (!MASK || (key0 + HALF < whi && key0 + BN > wlo));
         if (MASK) {
             if (have_p) st.pv(vcur, 0, s);
@@ -546,6 +574,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
         }
         lds_barrier();
         // ---- V(2j+1)
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
         have_p = live1;
         if (live1) {
             float alpha[2];
@@ -568,7 +597,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
     // Last matrix phase: P.V of the final half.
     if (have_p) st.pv(vt0 + ((nsteps - 1) & 1) * TILE_BYTES, 1, s);
     lds_barrier();
-    if (grp == 0) lds_barrier();  // same barrier count for both groups
+    if (NG == 2 && grp == 0) lds_barrier();  // same barrier count for both groups
 
     if (!active) return;
     // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2.
@@ -594,7 +623,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_wide_kernel(const FwdParams p
     }
 }
 
-template <bool EXPLICIT, bool CAP, bool FIXED>
+template <int NG, bool EXPLICIT, bool CAP, bool FIXED>
 int launch(const FwdParams &p, hipStream_t stream) {
     PairMap pm;
     pm.units = (int)(p.B * p.Hkv);
@@ -603,11 +632,11 @@ int launch(const FwdParams &p, hipStream_t stream) {
     pm.xcd = pm.units % 8 == 0 ? 1 : 0;
     pm.upx = pm.xcd ? pm.units / 8 : pm.units;
     pm.npairs = (pm.upx * pm.rep + 1) / 2;
-    const int64_t wgs = (int64_t)pm.npairs * pm.n_qtiles * (pm.xcd ? 8 : 1);
+    const int64_t wgs = NG == 2 ? (int64_t)pm.npairs * pm.n_qtiles * (pm.xcd ? 8 : 1) : p.B * p.H * pm.n_qtiles;
     if (wgs <= 0) return FA_OK;
     if (wgs > 0x7fffffff) return FA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((fwd_bf16_wide_kernel<EXPLICIT, CAP, FIXED>), dim3((unsigned)wgs), dim3(512), 0, stream, p,
-                       pm);
+    hipLaunchKernelGGL((fwd_bf16_wide_kernel<NG, EXPLICIT, CAP, FIXED>), dim3((unsigned)wgs), dim3(NG * 256), 0, stream,
+                       p, pm);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -623,11 +652,17 @@ bool fwd_bf16_wide_applies(const FwdParams &p, int d) {
 
 int launch_fwd_bf16_wide(const FwdParams &p, hipStream_t stream) {
     if (p.softcap > 0.0f) {
-        if (p.softcap <= kFixedMaxCap) return launch<true, true, true>(p, stream);
-        return launch<true, true, false>(p, stream);
+        if (p.softcap <= kFixedMaxCap) return launch<2, true, true, true>(p, stream);
+        return launch<2, true, true, false>(p, stream);
     }
-    if (!(p.scale > 0.0f)) return launch<true, false, false>(p, stream);
-    return launch<false, false, false>(p, stream);
+    bool windows = p.window > 0;
+    for (int h = 0; h < p.H && p.has_head_window; ++h) windows = windows || p.head_window[h] > 0;
+    if (windows) {
+        if (!(p.scale > 0.0f)) return launch<2, true, false, false>(p, stream);
+        return launch<2, false, false, false>(p, stream);
+    }
+    if (!(p.scale > 0.0f)) return launch<1, true, false, false>(p, stream);
+    return launch<1, false, false, false>(p, stream);
 }
 
 }  // namespace fa
