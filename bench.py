@@ -458,7 +458,7 @@ PROFILE_RUNS = {
     "copy_WRITE_SIZE": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_WRITE_SIZE -o run -- "
                        "python bench.py --copy-calibration",
 }
-KERNELS = {"prefill": "fwd_bf16_wide_kernel<false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
+KERNELS = {"prefill": "fwd_bf16_wide_kernel<1, false, false, false>", "decode": "splitkv_decode_kernel<128, 4, false>",
            "combine": "combine_few_kernel<128, 16>", "prefill_fp8": "fwd_fp8_kernel<128>",
            "rolling_decode": "splitkv_decode_kernel<128, 4, false>", "kv_append": "kv_append_kernel<128>",
            "softmax": "softmax_kernel<false, 4>", "topk": "softmax_topk_kernel<false, 4>",

@@ -516,11 +516,19 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
     f32x16 s[2];          // scores of a half, then (packed) its weights
     bool have_p = false;  // s holds weights of the previous half, not yet multiplied into O
 
-    // Tile step j: four phases, each ended by a workgroup barrier.
+    // Tile step j: four phases.
     //   M(2j):   loads of K_{j+1}; P.V of half (j-1, 1); scores of half (j, 0)
-    //   V(2j):   softmax of (j, 0); V_j (loaded at M(2j-1)) waited for
+    //   V(2j):   softmax of (j, 0)
     //   M(2j+1): loads of V_{j+1}; P.V of (j, 0); scores of (j, 1)
-    //   V(2j+1): softmax of (j, 1); K_{j+1} waited for
+    //   V(2j+1): softmax of (j, 1)
+    // NG = 2 ends every phase with a workgroup barrier (the barriers pace
+    // the ping-pong); V_j (loaded at M(2j-1)) is waited for in V(2j) and
+    // K_{j+1} in V(2j+1).  NG = 1 needs a barrier only after each matrix
+    // phase: a vector phase touches no LDS, so the barrier ending M(2j)
+    // both frees the buffers read there (V_{j-1}, whose slot V_{j+1} then
+    // fills) and publishes V_j, waited for just before it; likewise the
+    // barrier ending M(2j+1) frees K_j and publishes K_{j+1}.  A wave then
+    // goes from its vector phase straight into its next matrix phase.
     // Loads are waited for two or three phases after they are issued; the
     // wait for the older batch leaves the newer one (4 loads per wave) in
     // flight.  Tiles whose keys every valid row of the wave sees in full
@@ -546,6 +554,12 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
         } else {
             st.pv_scores(vprev, 1, kcur, 0, s);
         }
+        if (NG == 1 && mine) {
+            if (more)
+                __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): V_j's loads, not K_{j+1}'s
+            else
+                __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        }
         lds_barrier();
         // ---- V(2j)
         if (PRIO) __builtin_amdgcn_s_setprio(0);
@@ -555,13 +569,15 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
             if (st.template softmax<MASK>(s, kt, p, row0, W, alpha)) st.rescale(alpha);
             if (FIXED) st.sum_bf16_weights(s);
         }
-        if (mine) {
-            if (more)
-                __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): V_j's loads, not K_{j+1}'s
-            else
-                __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        if (NG == 2) {
+            if (mine) {
+                if (more)
+                    __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): V_j's loads, not K_{j+1}'s
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            }
+            lds_barrier();
         }
-        lds_barrier();
         // ---- M(2j+1)
         if (PRIO) __builtin_amdgcn_s_setprio(1);
         ld.load<true>(V, more ? head_bytes : 0u, glds_at + (VT0 + ((j + 1) & 1)) * TILE_BYTES, more ? kt + BN : 0);
@@ -572,6 +588,7 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
         } else {
             st.pv_scores(vcur, 0, kcur, 1, s);
         }
+        if (NG == 1 && more) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): K_{j+1}'s loads, not V_{j+1}'s
         lds_barrier();
         // ---- V(2j+1)
         if (PRIO) __builtin_amdgcn_s_setprio(0);
@@ -581,8 +598,10 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
             if (st.template softmax<MASK>(s, kt + HALF, p, row0, W, alpha)) st.rescale(alpha);
             if (FIXED) st.sum_bf16_weights(s);
         }
-        if (more) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): K_{j+1}'s loads, not V_{j+1}'s
-        lds_barrier();
+        if (NG == 2) {
+            if (more) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): K_{j+1}'s loads, not V_{j+1}'s
+            lds_barrier();
+        }
     };
     // Tiles [jf0, jf1) need no mask for this wave; the first of them runs
     // in the masked loop.
