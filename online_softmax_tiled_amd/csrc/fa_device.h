@@ -80,6 +80,14 @@ __device__ __forceinline__ float softcap_log2(float z, float kappa) {
     return (kappa * kLog2e) * t;
 }
 
+// The same from the raw product s, with the constants folded once per
+// launch: c2 = scale * 2 log2(e) / kappa, kl = kappa log2(e), nkl2 = -2 kl.
+// kl * tanh(u) = kl - 2 kl / (e^(2u) + 1): one multiply, exp2, add,
+// reciprocal and fused multiply-add per score.
+__device__ __forceinline__ float softcap_log2_pre(float s, float c2, float kl, float nkl2) {
+    return fmaf(__builtin_amdgcn_rcpf(fast_exp2(s * c2) + 1.0f), nkl2, kl);
+}
+
 // Visible-key interval [lo, hi) of a query at absolute position pos.
 __device__ __forceinline__ void key_bounds(int64_t pos, int64_t Nk, int causal, int window,
                                            int64_t &lo, int64_t &hi) {

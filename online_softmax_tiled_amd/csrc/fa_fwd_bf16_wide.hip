@@ -117,6 +117,7 @@ struct WideWave {
     float mu[2];                // the reference the weights are taken against (0 while m is -inf)
     float lx[2];                // FIXED: this lane's half of the sum of the fp32 weights (for lse)
     float c_log2, scale, softcap;
+    float cap_c2, cap_kl, cap_nkl2;  // soft-cap constants (softcap_log2_pre)
     // Lane-dependent offsets and mask bounds are recomputed from the lane id
     // where they are used: only the accumulators, Q^T and the row state stay
     // in registers through the loop.
@@ -222,7 +223,7 @@ struct WideWave {
             if (EXPLICIT) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
-                    s[rb][j] = CAP ? softcap_log2(s[rb][j] * scale, softcap) : s[rb][j] * c_log2;
+                    s[rb][j] = CAP ? softcap_log2_pre(s[rb][j], cap_c2, cap_kl, cap_nkl2) : s[rb][j] * c_log2;
             }
             if (MASK) {
                 // Key c + 4 hf of the half (c = 8 (j / 4) + j % 4) is visible
@@ -415,8 +416,10 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
     if (NG == 2) {
         has_b = pm.decode(blockIdx.x, p.causal, ua, ha, ub, hb, qtile);
     } else {
-        // One block per workgroup, in the XCD-aware order of decode_block.
-        const Work wk = decode_block(p, pm.n_qtiles);
+        // One block per workgroup, in the XCD-aware order of decode_block
+        // (two workgroups per CU: clusters of at least 128 blocks; measured
+        // on the causal workload 527.9 -> 523.6 us against 64).
+        const Work wk = decode_block(p, pm.n_qtiles, 128);
         qtile = wk.qtile;
         ua = wk.b * (int)p.Hkv + wk.h / pm.rep;
         ha = wk.h % pm.rep;
@@ -460,6 +463,9 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
     st.c_log2 = p.scale * kLog2e;
     st.scale = p.scale;
     st.softcap = p.softcap;
+    st.cap_kl = p.softcap * kLog2e;
+    st.cap_nkl2 = -2.0f * st.cap_kl;
+    st.cap_c2 = CAP ? p.scale * (2.0f * kLog2e) / p.softcap : 0.0f;
 
     // This wave's rows: row0 + 32 rb + l32.
     const int64_t row0 = q0 + RW * wi;

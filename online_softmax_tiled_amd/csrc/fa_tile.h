@@ -117,7 +117,7 @@ struct Work {
     int qtile, h, b, split;
 };
 
-__device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
+__device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles, int cluster_blocks = 64) {
     const int bid = blockIdx.x;
     const int rep = p.group, S = p.num_splits;
     const int units = (int)(p.B * p.Hkv);
@@ -129,14 +129,15 @@ __device__ __forceinline__ Work decode_block(const FwdParams &p, int n_qtiles) {
         // first across the cluster's units, so short tiles fill in at the
         // end of each cluster (one unit at a time, longest first, left the
         // last unit's long tiles in the tail).  C is the fewest units whose
-        // blocks reach twice the XCD's 32 resident workgroups: enough to
-        // balance, while only about C units' K and V are live in the XCD's
-        // L2 at a time (ordering across all units at once multiplied the
-        // HBM reads of K and V).
+        // blocks reach cluster_blocks, about twice the workgroups an XCD
+        // holds at once (64 for one workgroup per CU, 128 for two): enough
+        // to balance, while only about C units' K and V are live in the
+        // XCD's L2 at a time (ordering across all units at once multiplied
+        // the HBM reads of K and V).
         const int x = bid & 7, s = bid >> 3;
         const int upx = units / 8;
         const int unit_blocks = per_unit;
-        const int C = min(upx, max(1, (64 + unit_blocks - 1) / unit_blocks));
+        const int C = min(upx, max(1, (cluster_blocks + unit_blocks - 1) / unit_blocks));
         const int c0 = (s / (C * unit_blocks)) * C;
         const int csz = min(C, upx - c0);
         const int rem = s - c0 * unit_blocks;
