@@ -11,14 +11,16 @@
 // launch, where workgroups of 128 or 256 query rows would occupy a quarter
 // of them, and it needs no workspace: the partial results meet in LDS.
 //
-// Per wave and 32-key step: S^T = K Q^T (K operands loaded from HBM / L2
-// straight into registers, one 16-byte load per lane and 16 dims), the
-// online softmax of its 32 x 32 block (lazily moved reference maximum, as
-// in the other kernels), P rounded to
-// bf16, and O^T += V^T P^T with the V^T operands read from a row-major
-// staging copy of the step's V rows in the wave's own LDS slot
-// (transposing reads, ds_read_b64_tr_b16).  The next three steps' K and V
-// are in flight while a step computes.
+// Per wave and 32-key step: the step's K and V rows go from HBM / L2
+// straight into the wave's own LDS slots (coalesced 1 KiB loads; K rows
+// swizzled so that the operand reads are free of bank conflicts), S^T = K
+// Q^T with K operands read back from LDS, the online softmax of its 32 x 32
+// block (lazily moved reference maximum, as in the other kernels), P
+// rounded to bf16, and O^T += V^T P^T with the V^T operands read from the
+// row-major V rows (transposing reads, ds_read_b64_tr_b16).  The next
+// step's K and V are in flight while a step computes.  (K loaded straight
+// into registers in operand layout touches 32 rows per load instruction;
+// through LDS the B=1, H=8, 1024^2, d=64 launch went from 11.5 to 9.1 us.)
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_tile.h"
@@ -60,12 +62,20 @@ template <int D>
 struct SkLayout {
     static constexpr int SK_WAVES = sk_waves<D>();
     static constexpr int ROW_BYTES = D * 2;
-    static constexpr int VBUF = SK_STEP * ROW_BYTES;              // one step of V rows (bytes)
-    static constexpr int SLOTS = 4;                               // steps of V in flight
-    static constexpr int WAVE_BYTES = SLOTS * VBUF;
+    static constexpr int VBUF = SK_STEP * ROW_BYTES;              // one step of V (or K) rows (bytes)
+    static constexpr int SLOTS = 2;                               // steps of K and V in flight
+    static constexpr int WAVE_BYTES = SLOTS * 2 * VBUF;           // K slots, then V slots
+    static constexpr int CPR = D / 8;                             // 16-byte chunks per row
+    static constexpr int RPL_LOG2 = D == 128 ? 0 : (D == 64 ? 1 : 2);  // log2(rows per 256-byte bank line)
+    // K: chunk c of row r in slot c ^ ((r >> RPL_LOG2) % CPR): the 16 rows
+    // of one 16-lane pass of an operand read land on distinct bank groups.
+    __device__ static int kslot(int r, int c) { return c ^ ((r >> RPL_LOG2) & (CPR - 1)); }
     static constexpr int STAGE = SK_WAVES * WAVE_BYTES;           // all waves
-    static constexpr int MERGE = SK_WAVES * SK_ROWS * (D + 2) * 4;  // O, m, l of every wave (fp32)
-    static constexpr int BYTES = STAGE > MERGE ? STAGE : MERGE;
+    // A wave's partial result (O [32][D], m [32], l [32], fp32) goes into its
+    // own staging region once its last step has read it.
+    static constexpr int PART = SK_ROWS * (D + 2) * 4;
+    static_assert(PART <= WAVE_BYTES, "the partial result must fit in the wave's staging region");
+    static constexpr int BYTES = STAGE;
     static constexpr int LOADS = SK_STEP * D / 8 / 64;            // 16-byte V loads per lane per step
 };
 
@@ -137,13 +147,17 @@ __global__ __launch_bounds__(64 * sk_waves<D>()) void fwd_bf16_splitk_kernel(con
     // K operands of a step: lane l holds key k0 + l % 32, dims 16 ds + 8 hf
     // .. +7.  Buffer loads: keys past the end of the head read as zero (the
     // scalar offset counts toward the range check), and no lane branches.
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)K, (short)0, (int)head_bytes,
-                                                                          0x00020000);
-    auto load_k = [&](int64_t k0, u32x4 (&kr)[D / 16]) {
+    // K rows k0 .. k0 + 31 into K slot `slot`: load u fills slot bytes
+    // 1024 u + 16 lane, i.e. row r = (1024 u + 16 lane) / (2 D) and chunk
+    // slot sl, which holds chunk sl ^ swizzle(r) of the row.
+    auto load_k = [&](int64_t k0, int slot) {
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds)
-            kr[ds] = __builtin_amdgcn_raw_buffer_load_b128(krs, l32 * (D * 2) + ds * 32 + hf * 16,
-                                                           (int)(k0 * (D * 2)), 0);
+        for (int u = 0; u < SL::LOADS; ++u) {
+            const int b = 1024 * u + 16 * lane;
+            const int r = b / SL::ROW_BYTES, sl = (b % SL::ROW_BYTES) / 16;
+            buffer_load_lds16_at(K, head_bytes, wl_at + (uint32_t)(slot * SL::VBUF + 1024 * u),
+                                 r * SL::ROW_BYTES + 16 * SL::kslot(r, sl), (uint32_t)(k0 * (D * 2)));
+        }
     };
     // V rows k0 .. k0 + 31 into buffer slot, row-major (16-byte chunk c of
     // the step at byte 16 c); rows past the end of the head read as zero.
@@ -151,35 +165,28 @@ __global__ __launch_bounds__(64 * sk_waves<D>()) void fwd_bf16_splitk_kernel(con
 #pragma unroll
         for (int u = 0; u < SL::LOADS; ++u) {
             const int c = 64 * u + lane;
-            buffer_load_lds16_at(V, head_bytes, wl_at + (uint32_t)(slot * SL::VBUF + 1024 * u), c * 16,
+            buffer_load_lds16_at(V, head_bytes, wl_at + (uint32_t)((SL::SLOTS + slot) * SL::VBUF + 1024 * u), c * 16,
                                  (uint32_t)(k0 * (D * 2)));
         }
     };
 
-    // Step t computes with the K operands in kc (V in slot t % 4) and
-    // prefetches step t + 3's into kn (slot (t + 3) % 4); the loop rotates
-    // four register sets instead of copying.
-    auto step = [&](int t, const u32x4 (&kc)[D / 16], u32x4 (&kn)[D / 16]) {
+    // Step t computes with K and V in slot t % 2 and then refills that
+    // slot with step t + 2; step t + 1's loads stay in flight meanwhile.
+    auto step = [&](int t) {
         const int64_t k0 = wbeg + (int64_t)t * SK_STEP;
-        if (t + 3 < nsteps) {
-            load_k(k0 + 3 * SK_STEP, kn);
-            load_v(k0 + 3 * SK_STEP, (t + 3) % 4);
-        }
-        // Wait for this step's K and V; the later steps' loads may stay in flight.
-        const int later = nsteps - 1 - t;
-        if (later >= 3)
-            __builtin_amdgcn_s_waitcnt(kV3);
-        else if (later == 2)
-            __builtin_amdgcn_s_waitcnt(kV2);
-        else if (later == 1)
-            __builtin_amdgcn_s_waitcnt(kV1);
+        const int slot = t & 1;
+        if (t + 1 < nsteps)
+            __builtin_amdgcn_s_waitcnt(kV1);  // step t's loads, not step t + 1's
         else
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         // S^T = K Q^T: key 8 (j / 4) + 4 hf + j % 4 of the step, row l % 32.
         f32x16 s = {};
+        const char *kb = wl + slot * SL::VBUF;
 #pragma unroll
-        for (int ds = 0; ds < D / 16; ++ds)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ds]), qf[ds], s, 0, 0, 0);
+        for (int ds = 0; ds < D / 16; ++ds) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(kb + l32 * SL::ROW_BYTES + 16 * SL::kslot(l32, 2 * ds + hf));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ds], s, 0, 0, 0);
+        }
         // Scale / soft-cap into log2 units; masks unless every row sees the
         // whole step (element j is key 8 (j / 4) + j % 4 + 4 hf of the step).
 #pragma unroll
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(64 * sk_waves<D>()) void fwd_bf16_splitk_kernel(con
         // 32 db + 16 (gq % 2) + 4 jj .. +3, and receives dim 32 db + 16 (gq %
         // 2) + i of the group's 4 keys: rd = 0 gives keys 4 hf + [0, 4) of
         // the k-step, rd = 1 keys 8 + 4 hf + [0, 4), the order of pk.
-        const char *vb = wl + (t % 4) * SL::VBUF;
+        const char *vb = wl + (SL::SLOTS + slot) * SL::VBUF;
         const int gq = lane >> 4, e = (lane >> 2) & 3, jj = lane & 3;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -240,47 +247,44 @@ __global__ __launch_bounds__(64 * sk_waves<D>()) void fwd_bf16_splitk_kernel(con
                                                                    __builtin_bit_cast(bf16x8, pk[ks]), oacc[db], 0, 0,
                                                                    0);
             }
-        // The slot read here is refilled by the next step: its reads must land first.
+        // The slot read here is refilled with step t + 2: its reads must land first.
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        if (t + 2 < nsteps) {
+            load_k(k0 + 2 * SK_STEP, slot);
+            load_v(k0 + 2 * SK_STEP, slot);
+        }
     };
-    u32x4 ka[D / 16], kb[D / 16], kc[D / 16], kd[D / 16];
     if (nsteps > 0) {
-        load_k(wbeg, ka);
+        load_k(wbeg, 0);
         load_v(wbeg, 0);
     }
     if (nsteps > 1) {
-        load_k(wbeg + SK_STEP, kb);
+        load_k(wbeg + SK_STEP, 1);
         load_v(wbeg + SK_STEP, 1);
     }
-    if (nsteps > 2) {
-        load_k(wbeg + 2 * SK_STEP, kc);
-        load_v(wbeg + 2 * SK_STEP, 2);
-    }
-    for (int t = 0; t < nsteps; t += 4) {
-        step(t, ka, kd);
-        if (t + 1 < nsteps) step(t + 1, kb, ka);
-        if (t + 2 < nsteps) step(t + 2, kc, kb);
-        if (t + 3 < nsteps) step(t + 3, kd, kc);
-    }
+    for (int t = 0; t < nsteps; ++t) step(t);
 
-    // ---- merge the four waves' (m, l, O) through LDS.
+    // ---- merge the waves' (m, l, O) through LDS.  Each wave writes its
+    // partial into its own staging region (its last step waited for its
+    // reads of it), so one barrier suffices.
     const float lr = row_sum(l);
-    __syncthreads();  // every wave is done with its staging slot
-    float *const mo = reinterpret_cast<float *>(lds);  // O_w [4][32][D], then m_w [4][32], l_w [4][32]
-    float *const mm = mo + SK_WAVES * SK_ROWS * D;
-    float *const ml = mm + SK_WAVES * SK_ROWS;
+    {
+        float *const po = reinterpret_cast<float *>(wl);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 v4 = {oacc[db][4 * q], oacc[db][4 * q + 1], oacc[db][4 * q + 2], oacc[db][4 * q + 3]};
-            *reinterpret_cast<f32x4 *>(mo + (w * SK_ROWS + l32) * D + 32 * db + 8 * q + 4 * hf) = v4;
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v4 = {oacc[db][4 * q], oacc[db][4 * q + 1], oacc[db][4 * q + 2], oacc[db][4 * q + 3]};
+                *reinterpret_cast<f32x4 *>(po + l32 * D + 32 * db + 8 * q + 4 * hf) = v4;
+            }
+        if (hf == 0) {
+            po[SK_ROWS * D + l32] = m;
+            po[SK_ROWS * D + SK_ROWS + l32] = lr;
         }
-    if (hf == 0) {
-        mm[w * SK_ROWS + l32] = m;
-        ml[w * SK_ROWS + l32] = lr;
     }
     __syncthreads();
+    // Wave ww's partial: O at part(ww), m at part(ww) + 32 D, l after m.
+    auto part = [&](int ww) { return reinterpret_cast<const float *>(lds + ww * SL::WAVE_BYTES); };
     // 32 rows x D/4 groups of 4 dims over the workgroup's threads.
     for (int item = tid; item < SK_ROWS * (D / 4); item += 64 * SK_WAVES) {
         const int r = item / (D / 4), c4 = item % (D / 4);
@@ -288,15 +292,16 @@ __global__ __launch_bounds__(64 * sk_waves<D>()) void fwd_bf16_splitk_kernel(con
         if (qrow >= Nq) continue;
         float mx = kNegInf;
 #pragma unroll
-        for (int ww = 0; ww < SK_WAVES; ++ww) mx = fmaxf(mx, mm[ww * SK_ROWS + r]);
+        for (int ww = 0; ww < SK_WAVES; ++ww) mx = fmaxf(mx, part(ww)[SK_ROWS * D + r]);
         float den = 0.0f;
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if (mx != kNegInf) {
 #pragma unroll
             for (int ww = 0; ww < SK_WAVES; ++ww) {
-                const float f = fast_exp2(mm[ww * SK_ROWS + r] - mx);  // 0 for a wave that saw no key
-                den += f * ml[ww * SK_ROWS + r];
-                const f32x4 o4 = *reinterpret_cast<const f32x4 *>(mo + (ww * SK_ROWS + r) * D + 4 * c4);
+                const float *pw = part(ww);
+                const float f = fast_exp2(pw[SK_ROWS * D + r] - mx);  // 0 for a wave that saw no key
+                den += f * pw[SK_ROWS * D + SK_ROWS + r];
+                const f32x4 o4 = *reinterpret_cast<const f32x4 *>(pw + r * D + 4 * c4);
                 acc += f * o4;
             }
         }
