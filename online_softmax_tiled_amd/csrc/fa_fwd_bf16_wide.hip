@@ -619,6 +619,9 @@ __global__ __launch_bounds__(NG * 256, 2 / NG) void fwd_bf16_wide_kernel(const F
     for (; j < lo_full; ++j) tile_step(j, std::true_type{});
     for (; j < hi_full; ++j) tile_step(j, std::false_type{});
     for (; j < nsteps; ++j) tile_step(j, std::true_type{});
+    // The last step's zero-size loads still write LDS: they must land
+    // before the workgroup's LDS can go to another workgroup.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     // Last matrix phase: P.V of the final half.
     if (have_p) st.pv(vt0 + ((nsteps - 1) & 1) * TILE_BYTES, 1, s);
     lds_barrier();

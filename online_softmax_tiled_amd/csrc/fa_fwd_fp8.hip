@@ -114,6 +114,17 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8 &a, const i32x8 &b, const
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max16v(const f32x16 &s) {
+    const float a = vmax3(s[0], s[1], s[2]), b = vmax3(s[3], s[4], s[5]), c = vmax3(s[6], s[7], s[8]);
+    const float d = vmax3(s[9], s[10], s[11]), e = vmax3(s[12], s[13], s[14]);
+    return vmax3(vmax3(a, b, c), vmax3(d, e, s[15]), a);
+}
+
 template <int D>
 struct Wave8 {
     using L = Lay8<D>;
@@ -165,11 +176,7 @@ struct Wave8 {
                     if (!((uint32_t)(c - base) < span)) sacc[kb][j] = kNegInf;
                 }
         }
-        float x = sacc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) x = fmaxf(x, sacc[kb][j]);
+        const float x = vmax3(max16v(sacc[0]), max16v(sacc[1]), sacc[0][0]);
         const float mt = row_max(x * c_log2);
         const bool move = __builtin_amdgcn_ballot_w64(mt > m + TAU) != 0;
         const float m_new = move ? fmaxf(m, mt) : m;
