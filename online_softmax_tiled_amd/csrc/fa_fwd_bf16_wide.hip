@@ -20,8 +20,9 @@
 // with its own K and V tiles in LDS (64 KiB).  Each wave alternates a
 // matrix phase (P.V of the previous 32-key half, then the scores of the
 // next one; MFMA and LDS reads only) and a vector phase (masks, exp2, row
-// sum, bf16 packing), with a group barrier after each.  Two waves share
-// each SIMD, in one of two workgroup forms (template parameter NG):
+// sum, bf16 packing), with workgroup barriers between phases (see the tile
+// step).  Two waves share each SIMD, in one of two workgroup forms
+// (template parameter NG):
 //   * NG = 1: a workgroup is one group, two workgroups per CU.  They run
 //     independently; a workgroup that ends leaves the CU to the other one
 //     while the next starts loading.  Used when every head sees the same
@@ -37,8 +38,8 @@
 // phases: the vector work of the other wave on the SIMD then fills the
 // gaps between MFMAs instead of delaying them (the older wave wins the
 // issue arbitration otherwise).
-// Within a group, K and V tiles go from HBM straight
-// into LDS (direct loads by the group's 4 waves, 16 keys each), row-major
+// Within a group, K and V tiles go from HBM straight into LDS (direct
+// loads by the group's 4 waves, 16 keys each), row-major
 // with swizzles against bank conflicts (fa_bf16_tile.h); the V^T operand of
 // P.V is read from the row-major V tile with transposing LDS reads, so V is
 // never transposed or copied inside LDS.
